@@ -1,0 +1,195 @@
+/*
+ * gqa_oracle.c -- plain, slow, fp64 CPU oracle for single-token grouped-query-attention decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the benchmark's CPU-baseline
+ * leg may load this library.  It shares no code, header, table or helper with the HIP library and
+ * must never be called on the product path.
+ *
+ * What it computes (written from the pages, not from any kernel):
+ *   - Scaled dot-product attention per query head, unchanged by grouping: score_t = (q . k_t) * scale,
+ *     softmax over the cached tokens, output = softmax-weighted sum of the value rows.
+ *     ("Grouped Query Attention (GQA): Efficient Multi-Head Attention", Worked example 2; "Llama-2 70B
+ *     uses 64 query heads ...", section "What stays the same".)
+ *   - Query head h reads KV head floor(h / G) with G = Hq / Hkv, i.e. contiguous groups of G query
+ *     heads share one K head and one V head.  ("Grouped-Query Attention: How Sharing KV Heads Shrinks
+ *     Inference Memory", section "How grouped-query attention works"; "GQA, decode the acronym ...";
+ *     "Llama-2 70B uses 64 query heads ...", section "What the choice does to attention".)
+ *   - The decode query attends to the cached K/V of the tokens already in the cache, here exactly the
+ *     first seq_lens[b] positions.  ("Grouped Query Attention (GQA): Efficient Multi-Head Attention",
+ *     section "The bottleneck: autoregressive decoding ...".)
+ *   - KV bytes per token = 2 * layers * kv_heads * head_dim * dtype_bytes.  ("Grouped Query Attention:
+ *     Why 8 KV Heads Decide Your Batch Size", section "Why does GQA decide your batch size?".)
+ *   - An fp8 KV cache stores 8-bit values with per-tensor scales; real value = stored * descale.
+ *     ("Grouped-Query Attention: How Sharing KV Heads Shrinks Inference Memory", section "FP8 KV cache:
+ *     the other factor of two".)  The 8-bit format is OCP e4m3fn, decoded here from its definition.
+ *
+ * Readings where the pages are silent: seq_len 0 yields an all-zero output row; seq_len outside [0, L]
+ * is an error (return code 2); the output is returned in fp64 so that the caller's comparison includes
+ * whatever rounding the device path applies.
+ *
+ * Every input element is decoded exactly to double; all accumulation is double, in plain index order.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_FP8_E4M3 = 2 };
+
+/* bf16 is the upper 16 bits of an IEEE binary32. */
+double gqa_oracle_bf16_to_double(uint16_t h) {
+  uint32_t u = ((uint32_t)h) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* OCP 8-bit e4m3fn: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent field 0 is
+ * subnormal (m * 2^-9); exponent 15 with mantissa 7 is NaN; there is no infinity. */
+double gqa_oracle_fp8_e4m3_to_double(uint8_t c) {
+  int sign = (c >> 7) & 1;
+  int e = (c >> 3) & 15;
+  int m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+static int elem_size(int dt) {
+  switch (dt) {
+    case ORACLE_F32: return 4;
+    case ORACLE_BF16: return 2;
+    case ORACLE_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+static double load_elem(const void* base, int dt, size_t idx) {
+  switch (dt) {
+    case ORACLE_F32: {
+      float f;
+      memcpy(&f, (const char*)base + idx * 4, 4);
+      return (double)f;
+    }
+    case ORACLE_BF16: {
+      uint16_t h;
+      memcpy(&h, (const char*)base + idx * 2, 2);
+      return gqa_oracle_bf16_to_double(h);
+    }
+    default: return gqa_oracle_fp8_e4m3_to_double(((const uint8_t*)base)[idx]);
+  }
+}
+
+uint64_t gqa_oracle_kv_bytes_per_token(uint64_t layers, uint64_t kv_heads, uint64_t head_dim,
+                                       uint64_t dtype_bytes) {
+  /* one K tensor and one V tensor per layer and per KV head */
+  return 2u * layers * kv_heads * head_dim * dtype_bytes;
+}
+
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  int q_dtype, kv_dtype;
+  double k_descale, v_descale, scale;
+  const int32_t* seq_lens;
+  int B, Hq, Hkv, L, d;
+} problem_t;
+
+static int check(const problem_t* p) {
+  if (p->B < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->L < 0 || p->d <= 0) return 1;
+  if (p->Hq % p->Hkv != 0) return 1;
+  if (!elem_size(p->q_dtype) || !elem_size(p->kv_dtype)) return 1;
+  for (int b = 0; b < p->B; ++b)
+    if (p->seq_lens[b] < 0 || p->seq_lens[b] > p->L) return 2;
+  return 0;
+}
+
+/* Softmax weights of query head (b, h) over its n cached tokens, written to w[0..n).  Returns n. */
+static int head_weights(const problem_t* p, int b, int h, double* w) {
+  const int G = p->Hq / p->Hkv;
+  const int j = h / G; /* contiguous grouping */
+  const int n = p->seq_lens[b];
+  const size_t qbase = ((size_t)b * p->Hq + h) * p->d;
+  const size_t kbase = ((size_t)b * p->Hkv + j) * (size_t)p->L * p->d;
+  if (n == 0) return 0;
+  double m = -INFINITY;
+  for (int t = 0; t < n; ++t) {
+    double dot = 0.0;
+    for (int c = 0; c < p->d; ++c)
+      dot += load_elem(p->q, p->q_dtype, qbase + c) *
+             (load_elem(p->k, p->kv_dtype, kbase + (size_t)t * p->d + c) * p->k_descale);
+    w[t] = dot * p->scale;
+    if (w[t] > m) m = w[t];
+  }
+  double z = 0.0;
+  for (int t = 0; t < n; ++t) {
+    w[t] = exp(w[t] - m);
+    z += w[t];
+  }
+  for (int t = 0; t < n; ++t) w[t] /= z;
+  return n;
+}
+
+static void head_output(const problem_t* p, int b, int h, double* w, double* out_row) {
+  const int G = p->Hq / p->Hkv;
+  const int j = h / G;
+  const size_t vbase = ((size_t)b * p->Hkv + j) * (size_t)p->L * p->d;
+  const int n = head_weights(p, b, h, w);
+  for (int c = 0; c < p->d; ++c) {
+    double acc = 0.0;
+    for (int t = 0; t < n; ++t)
+      acc += w[t] * (load_elem(p->v, p->kv_dtype, vbase + (size_t)t * p->d + c) * p->v_descale);
+    out_row[c] = acc; /* n == 0 leaves the row at zero */
+  }
+}
+
+#define FILL_PROBLEM                                                                            \
+  problem_t p;                                                                                  \
+  p.q = q; p.k = k; p.v = v; p.q_dtype = q_dtype; p.kv_dtype = kv_dtype;                        \
+  p.k_descale = k_descale; p.v_descale = v_descale; p.scale = scale; p.seq_lens = seq_lens;     \
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.d = d;
+
+/* Full decode: out[B, Hq, d] (fp64).  w_scratch must hold L doubles.  Returns 0, 1 (bad shape or
+ * dtype) or 2 (a seq_len outside [0, L]). */
+int gqa_oracle_decode(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                      double k_descale, double v_descale, const int32_t* seq_lens, double scale,
+                      int B, int Hq, int Hkv, int L, int d, double* w_scratch, double* out) {
+  FILL_PROBLEM
+  int rc = check(&p);
+  if (rc) return rc;
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < Hq; ++h) head_output(&p, b, h, w_scratch, out + ((size_t)b * Hq + h) * d);
+  return 0;
+}
+
+/* Selected rows only: rows holds nrows pairs (b, h); out is [nrows, d]. */
+int gqa_oracle_decode_rows(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                           double k_descale, double v_descale, const int32_t* seq_lens, double scale,
+                           int B, int Hq, int Hkv, int L, int d, const int32_t* rows, int nrows,
+                           double* w_scratch, double* out) {
+  FILL_PROBLEM
+  int rc = check(&p);
+  if (rc) return rc;
+  for (int r = 0; r < nrows; ++r) {
+    int b = rows[2 * r], h = rows[2 * r + 1];
+    if (b < 0 || b >= B || h < 0 || h >= Hq) return 1;
+    head_output(&p, b, h, w_scratch, out + (size_t)r * d);
+  }
+  return 0;
+}
+
+/* Softmax weights of one query head (b, h): w[0..seq_lens[b]).  Returns the count, or -1/-2. */
+int gqa_oracle_weights(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                       double k_descale, double v_descale, const int32_t* seq_lens, double scale,
+                       int B, int Hq, int Hkv, int L, int d, int b, int h, double* w) {
+  FILL_PROBLEM
+  int rc = check(&p);
+  if (rc) return -rc;
+  if (b < 0 || b >= B || h < 0 || h >= Hq) return -1;
+  return head_weights(&p, b, h, w);
+}

@@ -1,0 +1,133 @@
+"""ctypes front end of the C oracle ``gqa_oracle.c`` (test infrastructure only).
+
+Inputs are passed as raw storage: float32 arrays for fp32, uint16 bit patterns for bf16 and uint8 codes
+for fp8-e4m3fn, together with a dtype name.  torch CPU tensors are accepted and reinterpreted as that
+raw storage without any arithmetic.  Results come back as float64 numpy arrays.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+DTYPES = {"f32": 0, "bf16": 1, "fp8_e4m3": 2}
+_RAW = {"f32": np.float32, "bf16": np.uint16, "fp8_e4m3": np.uint8}
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        c_void, c_int, c_dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+        common = [c_void, c_int, c_void, c_void, c_int, c_dbl, c_dbl, c_void, c_dbl,
+                  c_int, c_int, c_int, c_int, c_int]
+        L.gqa_oracle_decode.argtypes = common + [c_void, c_void]
+        L.gqa_oracle_decode.restype = c_int
+        L.gqa_oracle_decode_rows.argtypes = common + [c_void, c_int, c_void, c_void]
+        L.gqa_oracle_decode_rows.restype = c_int
+        L.gqa_oracle_weights.argtypes = common + [c_int, c_int, c_void]
+        L.gqa_oracle_weights.restype = c_int
+        L.gqa_oracle_kv_bytes_per_token.argtypes = [ctypes.c_uint64] * 4
+        L.gqa_oracle_kv_bytes_per_token.restype = ctypes.c_uint64
+        L.gqa_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.gqa_oracle_bf16_to_double.restype = c_dbl
+        L.gqa_oracle_fp8_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.gqa_oracle_fp8_e4m3_to_double.restype = c_dbl
+        _lib = L
+    return _lib
+
+
+def raw(x, dtype_name):
+    """Contiguous numpy view of the storage of x, reinterpreted as the raw type of dtype_name."""
+    want = _RAW[dtype_name]
+    if hasattr(x, "detach"):  # torch tensor
+        import torch
+
+        x = x.detach().cpu().contiguous()
+        as_int = {np.uint16: torch.int16, np.uint8: torch.uint8, np.float32: torch.float32}[want]
+        x = x.view(as_int).numpy().view(want)
+    a = np.ascontiguousarray(x)
+    if a.dtype != want:
+        raise TypeError(f"{dtype_name} storage must be {np.dtype(want)}, got {a.dtype}")
+    return a
+
+
+def _args(q, k, v, seq_lens, scale, q_dtype, kv_dtype, k_descale, v_descale):
+    qa, ka, va = raw(q, q_dtype), raw(k, kv_dtype), raw(v, kv_dtype)
+    if qa.ndim != 3 or ka.ndim != 4 or va.shape != ka.shape:
+        raise ValueError("q must be [B,Hq,d]; k and v [B,Hkv,L,d]")
+    B, Hq, d = qa.shape
+    Bk, Hkv, L, dk = ka.shape
+    if Bk != B or dk != d:
+        raise ValueError("batch or head_dim mismatch between q and the cache")
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32).reshape(-1))
+    if sl.shape[0] != B:
+        raise ValueError("seq_lens must have B entries")
+    keep = (qa, ka, va, sl)
+    args = [qa.ctypes.data, DTYPES[q_dtype], ka.ctypes.data, va.ctypes.data, DTYPES[kv_dtype],
+            float(k_descale), float(v_descale), sl.ctypes.data, float(scale), B, Hq, Hkv, L, d]
+    return args, keep, (B, Hq, Hkv, L, d)
+
+
+def _raise(rc):
+    if rc == 1:
+        raise ValueError("oracle: invalid shape or dtype")
+    if rc == 2:
+        raise ValueError("oracle: a seq_len lies outside [0, L]")
+    if rc:
+        raise RuntimeError(f"oracle: error {rc}")
+
+
+def decode(q, k, v, seq_lens, scale, q_dtype="f32", kv_dtype="f32", k_descale=1.0, v_descale=1.0):
+    """out[B, Hq, d] in float64."""
+    args, keep, (B, Hq, Hkv, L, d) = _args(q, k, v, seq_lens, scale, q_dtype, kv_dtype, k_descale,
+                                           v_descale)
+    out = np.zeros((B, Hq, d), dtype=np.float64)
+    w = np.zeros(max(L, 1), dtype=np.float64)
+    _raise(lib().gqa_oracle_decode(*args, w.ctypes.data, out.ctypes.data))
+    del keep
+    return out
+
+
+def decode_rows(q, k, v, seq_lens, scale, rows, q_dtype="f32", kv_dtype="f32", k_descale=1.0,
+                v_descale=1.0):
+    """Only the listed (b, h) rows: returns [len(rows), d] float64."""
+    args, keep, (B, Hq, Hkv, L, d) = _args(q, k, v, seq_lens, scale, q_dtype, kv_dtype, k_descale,
+                                           v_descale)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+    out = np.zeros((r.shape[0], d), dtype=np.float64)
+    w = np.zeros(max(L, 1), dtype=np.float64)
+    _raise(lib().gqa_oracle_decode_rows(*args, r.ctypes.data, r.shape[0], w.ctypes.data,
+                                        out.ctypes.data))
+    del keep
+    return out
+
+
+def weights(q, k, v, seq_lens, scale, b, h, q_dtype="f32", kv_dtype="f32", k_descale=1.0,
+            v_descale=1.0):
+    """Softmax weights of query head (b, h) over its seq_lens[b] tokens (float64)."""
+    args, keep, (B, Hq, Hkv, L, d) = _args(q, k, v, seq_lens, scale, q_dtype, kv_dtype, k_descale,
+                                           v_descale)
+    w = np.zeros(max(L, 1), dtype=np.float64)
+    n = lib().gqa_oracle_weights(*args, int(b), int(h), w.ctypes.data)
+    if n < 0:
+        _raise(-n)
+    del keep
+    return w[:n].copy()
+
+
+def kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes=2):
+    return int(lib().gqa_oracle_kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes))
+
+
+def bf16_to_double(bits):
+    return lib().gqa_oracle_bf16_to_double(int(bits))
+
+
+def fp8_e4m3_to_double(code):
+    return lib().gqa_oracle_fp8_e4m3_to_double(int(code))
