@@ -1,0 +1,221 @@
+// gqa_api.hip -- host side of libgqa: argument validation, split-K planning, workspace layout and
+// kernel dispatch.  Every entry point declared in include/gqa.h is defined here.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "gqa.h"
+#include "gqa_kernels.h"
+
+namespace {
+
+constexpr int kWaves = 4;             // waves per workgroup
+constexpr int kChunkQuantum = 256;    // chunk lengths are multiples of this many tokens
+constexpr int kTargetWorkgroups = 2048;  // 8 per compute unit on a 256-CU MI355X
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int elt_bytes(int dt) { return dt == GQA_F32 ? 4 : dt == GQA_BF16 ? 2 : 1; }
+bool known_dtype(int dt) { return dt == GQA_F32 || dt == GQA_BF16 || dt == GQA_FP8_E4M3; }
+
+// Split-K chunk length: the largest multiple of 256 tokens that still yields about
+// kTargetWorkgroups (batch, KV head, chunk) work items, so that every CU gets several and the
+// per-chunk partial results stay a small fraction of the cache bytes.
+int plan_chunk(const gqa_shape_t* s) {
+  if (s->chunk_tokens > 0) return s->chunk_tokens;
+  const long long units = (long long)s->B * s->Hkv;
+  for (int c = 4096; c > kChunkQuantum; c /= 2) {
+    const long long nc = (s->L + c - 1) / c;
+    if (units * nc >= kTargetWorkgroups) return c;
+  }
+  return kChunkQuantum;
+}
+
+struct Layout {
+  int chunk, nchunks;
+  size_t counters_off, ml_off, o_off, total;
+};
+
+Layout plan(const gqa_shape_t* s) {
+  Layout lo;
+  lo.chunk = plan_chunk(s);
+  lo.nchunks = (s->L + lo.chunk - 1) / lo.chunk;
+  const size_t units = (size_t)s->B * s->Hkv;
+  const size_t G = (size_t)(s->Hq / s->Hkv);
+  lo.counters_off = 0;
+  lo.ml_off = align_up(units * sizeof(uint32_t));
+  lo.o_off = lo.ml_off + align_up(units * lo.nchunks * G * 2 * sizeof(float));
+  lo.total = lo.o_off + align_up(units * lo.nchunks * G * (size_t)s->d * sizeof(float));
+  return lo;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+template <typename K>
+gqa_status_t launch(K kernel, int grid, const gqa::Params& prm, hipStream_t stream) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWaves * 64), 0, stream, prm);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+template <int D, int NT, bool FP8>
+gqa_status_t dispatch_mfma_out(int out_dtype, int grid, const gqa::Params& prm, hipStream_t st) {
+  if (out_dtype == GQA_BF16) return launch(gqa::decode_mfma_kernel<D, NT, FP8, uint16_t, kWaves>, grid, prm, st);
+  return launch(gqa::decode_mfma_kernel<D, NT, FP8, float, kWaves>, grid, prm, st);
+}
+
+template <int D, bool FP8>
+gqa_status_t dispatch_mfma(int G, int out_dtype, int grid, const gqa::Params& prm, hipStream_t st) {
+  if (G <= 16) return dispatch_mfma_out<D, 1, FP8>(out_dtype, grid, prm, st);
+  return dispatch_mfma_out<D, 2, FP8>(out_dtype, grid, prm, st);
+}
+
+template <int D, int GT>
+gqa_status_t dispatch_f32_out(int out_dtype, int grid, const gqa::Params& prm, hipStream_t st) {
+  if (out_dtype == GQA_BF16) return launch(gqa::decode_f32_kernel<D, GT, uint16_t, kWaves>, grid, prm, st);
+  return launch(gqa::decode_f32_kernel<D, GT, float, kWaves>, grid, prm, st);
+}
+
+template <int D>
+gqa_status_t dispatch_f32(int G, int out_dtype, int grid, const gqa::Params& prm, hipStream_t st) {
+  if (G <= 1) return dispatch_f32_out<D, 1>(out_dtype, grid, prm, st);
+  if (G <= 2) return dispatch_f32_out<D, 2>(out_dtype, grid, prm, st);
+  if (G <= 4) return dispatch_f32_out<D, 4>(out_dtype, grid, prm, st);
+  if (G <= 8) return dispatch_f32_out<D, 8>(out_dtype, grid, prm, st);
+  if (G <= 16) return dispatch_f32_out<D, 16>(out_dtype, grid, prm, st);
+  return dispatch_f32_out<D, 32>(out_dtype, grid, prm, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+gqa_status_t gqa_shape_check(const gqa_shape_t* s) {
+  if (!s) return GQA_ERR_INVALID_ARG;
+  if (s->B <= 0 || s->Hq <= 0 || s->Hkv <= 0 || s->L <= 0 || s->d <= 0) return GQA_ERR_INVALID_ARG;
+  if (s->Hq % s->Hkv != 0) return GQA_ERR_INVALID_ARG;
+  if (!known_dtype(s->q_dtype) || !known_dtype(s->kv_dtype) || !known_dtype(s->out_dtype))
+    return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(s->k_descale) || !std::isfinite(s->v_descale)) return GQA_ERR_INVALID_ARG;
+  if (s->chunk_tokens < 0 || s->chunk_tokens % kChunkQuantum != 0) return GQA_ERR_INVALID_ARG;
+  if (s->d != 64 && s->d != 128) return GQA_ERR_UNSUPPORTED;
+  if (s->Hq / s->Hkv > 32) return GQA_ERR_UNSUPPORTED;
+  if (s->out_dtype != GQA_F32 && s->out_dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
+  const bool f32_path = s->q_dtype == GQA_F32 && s->kv_dtype == GQA_F32;
+  const bool mfma_path = s->q_dtype == GQA_BF16 && (s->kv_dtype == GQA_BF16 || s->kv_dtype == GQA_FP8_E4M3);
+  if (!f32_path && !mfma_path) return GQA_ERR_UNSUPPORTED;
+  // per-(batch, KV head) cache slices are addressed with 32-bit byte offsets
+  if ((long long)s->L * s->d * elt_bytes(s->kv_dtype) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
+  const long long c = plan_chunk(s);
+  if ((long long)s->B * s->Hkv * ((s->L + c - 1) / c) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
+  if ((long long)s->B * s->Hq >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+size_t gqa_decode_workspace_bytes(const gqa_shape_t* s) {
+  if (gqa_shape_check(s) != GQA_OK) return 0;
+  return plan(s).total;
+}
+
+gqa_status_t gqa_workspace_init(void* workspace, size_t workspace_bytes, const gqa_shape_t* s,
+                                void* stream) {
+  const gqa_status_t st = gqa_shape_check(s);
+  if (st != GQA_OK) return st;
+  if (!workspace || !aligned(workspace, 16)) return GQA_ERR_INVALID_ARG;
+  const Layout lo = plan(s);
+  if (workspace_bytes < lo.total) return GQA_ERR_WORKSPACE;
+  const int n = s->B * s->Hkv;
+  hipLaunchKernelGGL(gqa::clear_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<uint32_t*>(workspace), n);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, float scale, void* out, const gqa_shape_t* s,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !out || !s) return GQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(seq_lens, 4))
+    return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  const gqa_status_t st = gqa_shape_check(s);
+  if (st != GQA_OK) return st;
+  const Layout lo = plan(s);
+  if (!workspace || workspace_bytes < lo.total) return GQA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return GQA_ERR_INVALID_ARG;
+
+  gqa::Params prm;
+  prm.q = q;
+  prm.k = k_cache;
+  prm.v = v_cache;
+  prm.seq_lens = seq_lens;
+  prm.out = out;
+  char* ws = static_cast<char*>(workspace);
+  prm.counters = reinterpret_cast<uint32_t*>(ws + lo.counters_off);
+  prm.part_ml = reinterpret_cast<float*>(ws + lo.ml_off);
+  prm.part_o = reinterpret_cast<float*>(ws + lo.o_off);
+  prm.B = s->B;
+  prm.Hq = s->Hq;
+  prm.Hkv = s->Hkv;
+  prm.L = s->L;
+  prm.G = s->Hq / s->Hkv;
+  prm.chunk = lo.chunk;
+  prm.nchunks = lo.nchunks;
+  prm.qk_scale = (float)((double)scale * (double)s->k_descale * 1.4426950408889634);
+  prm.v_descale = s->v_descale;
+
+  const int grid = s->B * s->Hkv * lo.nchunks;
+  hipStream_t hs = (hipStream_t)stream;
+  if (s->kv_dtype == GQA_F32) {
+    return s->d == 64 ? dispatch_f32<64>(prm.G, s->out_dtype, grid, prm, hs)
+                      : dispatch_f32<128>(prm.G, s->out_dtype, grid, prm, hs);
+  }
+  if (s->kv_dtype == GQA_BF16) {
+    return s->d == 64 ? dispatch_mfma<64, false>(prm.G, s->out_dtype, grid, prm, hs)
+                      : dispatch_mfma<128, false>(prm.G, s->out_dtype, grid, prm, hs);
+  }
+  return s->d == 64 ? dispatch_mfma<64, true>(prm.G, s->out_dtype, grid, prm, hs)
+                    : dispatch_mfma<128, true>(prm.G, s->out_dtype, grid, prm, hs);
+}
+
+uint64_t gqa_kv_bytes_per_token(uint32_t layers, uint32_t kv_heads, uint32_t head_dim,
+                                uint32_t dtype_bytes) {
+  return (uint64_t)2 * layers * kv_heads * head_dim * dtype_bytes;
+}
+
+gqa_status_t gqa_validate_seq_lens(const int32_t* seq_lens, int32_t B, int32_t L,
+                                   int32_t* bad_count, void* stream) {
+  if (!seq_lens || !bad_count || B <= 0 || L < 0 || !aligned(seq_lens, 4) || !aligned(bad_count, 4))
+    return GQA_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(gqa::count_bad_seq_lens_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     seq_lens, B, L, bad_count);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+size_t gqa_stream_read_sink_words(void) { return 4096; }
+
+gqa_status_t gqa_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !aligned(src, 16) || !aligned(sink, 4))
+    return GQA_ERR_INVALID_ARG;
+  const size_t n16 = bytes / 16;
+  const int grid = 1024;
+  const size_t per_wg = (n16 + grid - 1) / grid;
+  hipLaunchKernelGGL(gqa::stream_read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                     static_cast<const gqa::u32x4_t*>(src), n16, per_wg, static_cast<uint32_t*>(sink));
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+const char* gqa_status_string(gqa_status_t status) {
+  switch (status) {
+    case GQA_OK: return "GQA_OK: success";
+    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG: null or misaligned pointer, bad dimension, Hq not a multiple of Hkv, bad chunk length or size overflow";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: head dim, group size, dtype combination or size outside what the library implements";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or smaller than gqa_decode_workspace_bytes()";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP: the HIP runtime reported an error while enqueueing";
+  }
+  return "unknown gqa_status_t";
+}
+
+}  // extern "C"

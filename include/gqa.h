@@ -1,0 +1,115 @@
+/*
+ * gqa.h -- C ABI of libgqa: single-token grouped-query-attention (GQA) decode over a KV cache on
+ * AMD MI355X (gfx950).
+ *
+ * The operation.  For every batch entry b and query head h, with G = Hq / Hkv and j = floor(h / G):
+ *
+ *     s_t        = scale * k_descale * dot(q[b,h,:], k_cache[b,j,t,:])     for t in [0, seq_lens[b])
+ *     out[b,h,:] = v_descale * sum_t softmax(s)_t * v_cache[b,j,t,:]
+ *
+ * i.e. ordinary scaled dot-product attention per query head, where each contiguous group of G query
+ * heads shares one K head and one V head ("Grouped-Query Attention: How Sharing KV Heads Shrinks
+ * Inference Memory", section "How grouped-query attention works"; "Grouped Query Attention (GQA):
+ * Efficient Multi-Head Attention", Worked example 2).  One decode step attends over the cached K/V
+ * of the tokens already in the cache ("Grouped Query Attention (GQA): Efficient Multi-Head
+ * Attention", section "The bottleneck: autoregressive decoding ..."); here those are exactly the first
+ * seq_lens[b] positions of the cache, and appending the new token is the caller's job.  A sequence
+ * with seq_lens[b] == 0 gets an all-zero output row.  The cache is read once per KV head for all G
+ * query heads of its group; nothing is expanded to Hq heads ("Grouped Query Attention: Why 8 KV
+ * Heads Decide Your Batch Size", sections "Why does GQA speed up decode, not just save memory?" and
+ * "Why doesn't GQA speed up my fine-tuned model?").
+ *
+ * Memory layout (all row-major, contiguous, device memory, 16-byte aligned base pointers):
+ *     q        [B, Hq, d]        dtype q_dtype
+ *     k_cache  [B, Hkv, L, d]    dtype kv_dtype   (L = allocated cache length per sequence)
+ *     v_cache  [B, Hkv, L, d]    dtype kv_dtype
+ *     seq_lens [B]               int32, each in [0, L] (values outside are clamped on the device)
+ *     out      [B, Hq, d]        dtype out_dtype
+ *
+ * Supported dtype combinations (q / kv / out): f32 / f32 / {f32, bf16}; bf16 / bf16 / {bf16, f32};
+ * bf16 / fp8-e4m3 / {bf16, f32}.  The fp8 cache is the OCP e4m3fn format with per-tensor descales
+ * (real value = stored * descale), as in "Grouped-Query Attention: How Sharing KV Heads Shrinks
+ * Inference Memory", section "FP8 KV cache: the other factor of two".  Head dims: 64 and 128.
+ * Group sizes: G = Hq / Hkv in [1, 32].  Accumulation is fp32; a bf16 out is rounded to nearest even.
+ *
+ * Ownership and threading.  The caller owns every buffer, the workspace included.  The library never
+ * allocates or frees device memory and keeps no mutable global state besides cached device
+ * attributes.  gqa_decode only enqueues work on the given stream and returns; it never synchronises.
+ * Two calls that run at the same time must not share a workspace.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1, GQA_FP8_E4M3 = 2 } gqa_dtype_t;
+
+typedef enum {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, bad dimension, Hq % Hkv != 0, overflow */
+  GQA_ERR_UNSUPPORTED = 2, /* head dim, group size or dtype combination outside the list above */
+  GQA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than gqa_decode_workspace_bytes() */
+  GQA_ERR_HIP = 4          /* the HIP runtime reported an error while enqueueing */
+} gqa_status_t;
+
+typedef struct {
+  int32_t B, Hq, Hkv, L, d;
+  int32_t q_dtype, kv_dtype, out_dtype; /* gqa_dtype_t values */
+  float k_descale, v_descale;           /* 1.0 for f32 and bf16 caches */
+  int32_t chunk_tokens; /* split-K chunk length in tokens: 0 = library's choice, else a positive
+                           multiple of 256 */
+} gqa_shape_t;
+
+/* Validates a shape (dimensions, divisibility, dtypes, chunk length, 32-bit per-head offsets).
+ * Host only; no HIP call.  Returns GQA_OK, GQA_ERR_INVALID_ARG or GQA_ERR_UNSUPPORTED. */
+gqa_status_t gqa_shape_check(const gqa_shape_t* shape);
+
+/* Bytes of device workspace gqa_decode needs for this shape (split-K partial results and one
+ * counter per (batch, KV head)); 0 if the shape is invalid.  Host only. */
+size_t gqa_decode_workspace_bytes(const gqa_shape_t* shape);
+
+/* Clears the counter part of a workspace.  A workspace must have been cleared once (by this call or
+ * by zero-filling it) before its first gqa_decode; every gqa_decode that completes leaves the
+ * counters at zero again.  Enqueues one small kernel on `stream` (a hipStream_t, NULL = default). */
+gqa_status_t gqa_workspace_init(void* workspace, size_t workspace_bytes, const gqa_shape_t* shape,
+                                void* stream);
+
+/* Enqueues the decode described at the top of this header on `stream` (a hipStream_t; NULL = the
+ * default stream).  scale is typically 1/sqrt(d) ("Grouped Query Attention (GQA): Efficient
+ * Multi-Head Attention", Worked example 2) and must be finite.  All checks that do not need device
+ * data run first and return an error before any HIP call; seq_lens is read on the device only. */
+gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, float scale, void* out, const gqa_shape_t* shape,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* KV-cache bytes per token: 2 (one K and one V tensor) * layers * kv_heads * head_dim * dtype_bytes
+ * ("Grouped Query Attention: Why 8 KV Heads Decide Your Batch Size", section "Why does GQA decide
+ * your batch size?").  Computed in 64-bit; host only. */
+uint64_t gqa_kv_bytes_per_token(uint32_t layers, uint32_t kv_heads, uint32_t head_dim,
+                                uint32_t dtype_bytes);
+
+/* Test helper: writes the number of seq_lens entries outside [0, L] to *bad_count (device memory).
+ * Enqueued on `stream`; does not synchronise.  Returns GQA_ERR_INVALID_ARG for null or misaligned
+ * pointers or B <= 0. */
+gqa_status_t gqa_validate_seq_lens(const int32_t* seq_lens, int32_t B, int32_t L, int32_t* bad_count,
+                                   void* stream);
+
+/* Measurement helper: streams `bytes` (a multiple of 16, 16-byte aligned) from `src` with
+ * non-temporal 16-byte loads and writes one 32-bit word per workgroup into `sink` (at least
+ * gqa_stream_read_sink_words() words).  Used to calibrate achievable read bandwidth. */
+gqa_status_t gqa_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+size_t gqa_stream_read_sink_words(void);
+
+/* Static description of a status code. */
+const char* gqa_status_string(gqa_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

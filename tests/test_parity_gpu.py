@@ -1,0 +1,346 @@
+"""GPU parity of libgqa against the fp64 CPU oracle, through the C ABI.
+
+Gates (max abs error vs the oracle on the same stored bytes): 1e-5 for an f32 cache, 1e-2 for bf16,
+5e-2 for fp8-e4m3.  Because outputs of N(0,1) data shrink like 1/sqrt(n), every comparison also
+gates the error relative to the reference's own scale (max and rms), which an all-zero or a
+token-dropping output would fail.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_attention_04_amd as gqa
+import workloads
+from oracle import ref
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ABS_GATE = {"f32": 1e-5, "bf16": 1e-2, "fp8_e4m3": 5e-2}
+MAX_REL_GATE = {"f32": 1e-5, "bf16": 1e-2, "fp8_e4m3": 1e-2}
+RMS_REL_GATE = {"f32": 2e-6, "bf16": 4e-3, "fp8_e4m3": 4e-3}
+TORCH = workloads.TORCH_DTYPES
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def to_dev(case):
+    return {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in case.items()}
+
+
+def run(case, out_dtype=None, chunk_tokens=0, scale=None):
+    d = to_dev(case)
+    od = TORCH[out_dtype or case["out_dtype"]]
+    out = gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"],
+                     case["scale"] if scale is None else scale, out_dtype=od,
+                     k_descale=case["k_descale"], v_descale=case["v_descale"],
+                     chunk_tokens=chunk_tokens)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_full(case, scale=None):
+    return ref.decode(case["q"], case["k"], case["v"], case["seq_lens"].numpy(),
+                      case["scale"] if scale is None else scale, case["q_dtype"], case["kv_dtype"],
+                      case["k_descale"], case["v_descale"])
+
+
+def compare(got, want, kv_dtype, label=""):
+    got = got.double().cpu().numpy().reshape(want.shape)
+    err = np.abs(got - want)
+    scale_max = max(np.abs(want).max(), 1e-30)
+    scale_rms = max(math.sqrt((want ** 2).mean()), 1e-30)
+    max_abs = err.max()
+    max_rel = max_abs / scale_max
+    rms_rel = math.sqrt((err ** 2).mean()) / scale_rms
+    say(f"  {label}: max_abs {max_abs:.3e} max_rel {max_rel:.3e} rms_rel {rms_rel:.3e}")
+    assert np.isfinite(got).all(), "non-finite output"
+    assert max_abs <= ABS_GATE[kv_dtype], (label, max_abs)
+    assert max_rel <= MAX_REL_GATE[kv_dtype], (label, max_rel)
+    assert rms_rel <= RMS_REL_GATE[kv_dtype], (label, rms_rel)
+    return max_abs
+
+
+DTYPES = [("f32", "f32"), ("bf16", "bf16"), ("bf16", "fp8_e4m3")]
+
+
+# ------------------------------------------------------------------------------ worked example
+@pytest.mark.parametrize("qd,kd", DTYPES)
+def test_worked_example_2_on_gpu(qd, kd):
+    """The hand-traced four-head example, zero-padded from head dim 2 to 64 (extra dims add nothing)."""
+    say(f"worked example 2 on GPU q={qd} kv={kd}")
+    q = torch.zeros(1, 4, 64)
+    k = torch.zeros(1, 2, 2, 64)
+    v = torch.zeros(1, 2, 2, 64)
+    q[0, :, :2] = torch.tensor([[1., 0.], [0., 1.], [1., 1.], [1., -1.]])
+    k[0, :, :, :2] = torch.tensor([[[1., 0.], [0., 1.]], [[1., 1.], [1., -1.]]])
+    v[0, :, :, :2] = torch.tensor([[[2., 0.], [0., 2.]], [[1., 1.], [3., 3.]]])
+    case = dict(q=workloads.cast(q, qd), k=workloads.cast(k, kd), v=workloads.cast(v, kd),
+                seq_lens=torch.tensor([2], dtype=torch.int32), scale=1 / math.sqrt(2),
+                k_descale=1.0, v_descale=1.0, q_dtype=qd, kv_dtype=kd, out_dtype=qd)
+    got = run(case, out_dtype="f32").cpu().double().numpy()[0, :, :2]
+    printed = np.array([[1.3395, 0.6605], [0.6605, 1.3395], [1.3911, 1.3911], [2.6089, 2.6089]])
+    # printed to 4 decimals; the bf16/fp8 paths round the weights to bf16 before P V
+    tol = 5e-5 if qd == "f32" else 1e-2
+    np.testing.assert_allclose(got, printed, rtol=0, atol=tol)
+    assert (run(case, out_dtype="f32").cpu()[0, :, 2:] == 0).all()
+
+
+# ------------------------------------------------------------------------------ small shapes
+SMALL = [
+    # (B, Hq, Hkv, d, L, seq_lens, chunk)
+    (3, 16, 4, 128, 1100, (1100, 777, 33), 256),
+    (2, 8, 2, 64, 700, (700, 1), 256),
+    (2, 8, 8, 128, 600, (513, 600), 256),      # G = 1 (MHA)
+    (2, 32, 1, 128, 520, (520, 257), 256),     # G = 32 (MQA)
+    (2, 12, 4, 64, 300, (300, 299), 0),        # G = 3
+    (1, 10, 2, 128, 900, (899,), 512),         # G = 5
+    (2, 32, 2, 128, 1000, (1000, 640), 256),   # G = 16
+    (1, 64, 8, 128, 2048, (2048,), 0),
+]
+
+
+@pytest.mark.parametrize("qd,kd", DTYPES)
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}d{c[3]}L{c[4]}")
+def test_small_parity(cfg, qd, kd):
+    B, Hq, Hkv, d, L, sl, chunk = cfg
+    say(f"small parity {cfg} q={qd} kv={kd}")
+    case = workloads.make_case(B, Hq, Hkv, d, L, qd, kd, seq_lens=sl, seed=hash(cfg) % 10000)
+    want = oracle_full(case)
+    compare(run(case, chunk_tokens=chunk), want, kd, "native out")
+    compare(run(case, out_dtype="f32", chunk_tokens=chunk), want, kd, "f32 out")
+
+
+# ------------------------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("qd,kd", DTYPES)
+def test_seq_len_edges(qd, kd):
+    L = 600
+    sl = (0, 1, 31, 32, 33, 255, 256, 257, 511, 512, 513, L)
+    say(f"seq_len edges {sl} q={qd} kv={kd}")
+    case = workloads.make_case(len(sl), 16, 4, 128, L, qd, kd, seq_lens=sl, seed=77)
+    want = oracle_full(case)
+    got = run(case, out_dtype="f32", chunk_tokens=256)
+    assert (got[0] == 0).all()
+    compare(got, want, kd, "edges")
+
+
+@pytest.mark.parametrize("qd,kd", DTYPES)
+def test_padding_is_never_read(qd, kd):
+    say(f"NaN-poisoned padding q={qd} kv={kd}")
+    sl = (300, 33, 1)
+    case = workloads.make_case(3, 8, 2, 128, 512, qd, kd, seq_lens=sl, seed=5)
+    base = run(case, out_dtype="f32", chunk_tokens=256).clone()
+    for key in ("k", "v"):
+        t = case[key]
+        raw = t.view(torch.uint8) if kd == "fp8_e4m3" else t
+        for b, n in enumerate(sl):
+            if kd == "fp8_e4m3":
+                raw[b, :, n:] = 0x7F        # e4m3fn NaN code
+            else:
+                raw[b, :, n:] = float("nan")
+    got = run(case, out_dtype="f32", chunk_tokens=256)
+    assert torch.isfinite(got).all()
+    assert torch.equal(got, base)
+
+
+def test_constant_v_per_kv_head():
+    """Weights sum to one, so V constant per (b, KV head) comes out unchanged: j + 10 b."""
+    say("constant V per KV head")
+    B, Hq, Hkv, d, L = 3, 24, 3, 128, 800
+    case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", "bf16", seq_lens=(800, 517, 2), seed=9)
+    v = torch.zeros(B, Hkv, L, d)
+    for b in range(B):
+        for j in range(Hkv):
+            v[b, j] = j + 10 * b
+    case["v"] = v.to(torch.bfloat16)
+    got = run(case, out_dtype="f32", chunk_tokens=256).cpu().double()
+    G = Hq // Hkv
+    want = torch.tensor([[h // G + 10 * b for h in range(Hq)] for b in range(B)], dtype=torch.float64)
+    assert torch.allclose(got, want[:, :, None].expand_as(got), rtol=2e-6, atol=0)
+
+
+@pytest.mark.parametrize("qd,kd", DTYPES)
+def test_zero_query_gives_prefix_mean(qd, kd):
+    say(f"zero query q={qd} kv={kd}")
+    B, Hq, Hkv, d, L = 2, 8, 2, 64, 700
+    sl = (700, 300)
+    case = workloads.make_case(B, Hq, Hkv, d, L, qd, kd, seq_lens=sl, seed=4)
+    case["q"] = torch.zeros_like(case["q"])
+    t = torch.arange(L, dtype=torch.float32)
+    if kd != "f32":        # keep the values exact in bf16 and e4m3 (integers below 16)
+        t = t % 16
+    case["v"] = workloads.cast(t[None, None, :, None].expand(B, Hkv, L, d).contiguous(), kd)
+    got = run(case, out_dtype="f32", chunk_tokens=256).cpu().double()
+    compare(got, oracle_full(case), kd, "zero q")
+    if kd == "f32":
+        for b, n in enumerate(sl):
+            assert torch.allclose(got[b], torch.full_like(got[b], (n - 1) / 2), rtol=1e-5, atol=0)
+
+
+def test_single_token_returns_value_row():
+    say("single token")
+    case = workloads.make_case(2, 16, 4, 128, 300, "bf16", "bf16", seq_lens=(1, 1), seed=8)
+    got = run(case, out_dtype="f32").cpu()
+    for b in range(2):
+        for h in range(16):
+            assert torch.equal(got[b, h], case["v"][b, h // 4, 0].float())
+
+
+def test_needle_inside_prefix_and_decoy_outside():
+    say("needle and decoy")
+    B, Hq, Hkv, d, L, n = 1, 8, 1, 128, 1024, 700
+    case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", "bf16", seq_lens=(n,), seed=3)
+    qv = case["q"][0, 0].float()
+    case["q"][0, :] = case["q"][0, 0]
+    unit = qv / qv.norm()
+    k = case["k"].float() * 0.05
+    k[0, 0, n - 1] = unit * 60
+    k[0, 0, n] = unit * 120       # decoy beyond the valid prefix
+    case["k"] = k.to(torch.bfloat16)
+    got = run(case, out_dtype="f32", chunk_tokens=256).cpu()
+    for h in range(Hq):
+        assert torch.allclose(got[0, h], case["v"][0, 0, n - 1].float(), atol=2e-2)
+
+
+# ------------------------------------------------------------------------------ invariances
+@pytest.mark.parametrize("qd,kd", DTYPES)
+def test_chunk_length_invariance(qd, kd):
+    say(f"chunk invariance q={qd} kv={kd}")
+    case = workloads.make_case(2, 16, 4, 128, 2048, qd, kd, seq_lens=(2048, 1500), seed=21)
+    outs = [run(case, out_dtype="f32", chunk_tokens=c).cpu().double() for c in (256, 512, 1024, 2048)]
+    ref_scale = outs[-1].abs().max()
+    # The f32 path carries the softmax weights in f32, so the split and merge must agree to f32
+    # rounding.  The matrix-core paths round each weight to bf16 against the running max of its own
+    # chunk, so different chunkings differ by up to about one bf16 unit (2^-8) of the output scale.
+    tol = 2e-5 if kd == "f32" else 2 ** -8
+    for o in outs[:-1]:
+        assert (o - outs[-1]).abs().max() <= tol * ref_scale
+    compare(outs[0], oracle_full(case), kd, "chunk 256")
+
+
+def test_bitwise_determinism_and_batch_independence():
+    say("determinism")
+    case = workloads.make_case(4, 32, 8, 128, 3000, "bf16", "bf16", seq_lens=(3000, 2222, 17, 1999),
+                               seed=31)
+    a = run(case).clone()
+    b = run(case).clone()
+    assert torch.equal(a, b)
+    case["k"][1] = torch.randn(case["k"][1].shape).to(torch.bfloat16)
+    case["v"][3] = 0
+    c = run(case)
+    assert torch.equal(a[0], c[0]) and torch.equal(a[2], c[2])
+
+
+def test_token_permutation_invariance():
+    say("permutation")
+    n = 1000
+    case = workloads.make_case(1, 16, 2, 128, 1024, "bf16", "bf16", seq_lens=(n,), seed=2)
+    a = run(case, out_dtype="f32", chunk_tokens=256).cpu().double()
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(0))
+    case["k"][0, :, :n] = case["k"][0, :, perm]
+    case["v"][0, :, :n] = case["v"][0, :, perm]
+    b = run(case, out_dtype="f32", chunk_tokens=256).cpu().double()
+    assert (a - b).abs().max() <= 5e-3 * a.abs().max()
+
+
+def test_bf16_output_is_rne_of_f32_output():
+    say("bf16 rounding")
+    case = workloads.make_case(3, 32, 8, 128, 1500, "bf16", "bf16", seq_lens=(1500, 900, 3), seed=12)
+    f = run(case, out_dtype="f32").cpu()
+    h = run(case, out_dtype="bf16").cpu()
+    assert torch.equal(f.to(torch.bfloat16).view(torch.int16), h.view(torch.int16))
+
+
+# ------------------------------------------------------------------------------ memory hygiene
+def test_output_guards_and_workspace_counters():
+    say("guards")
+    case = workloads.make_case(2, 16, 4, 128, 1200, "bf16", "bf16", seq_lens=(1200, 700), seed=6)
+    d = to_dev(case)
+    n = 2 * 16 * 128
+    buf = torch.full((n + 2 * 4096,), -7.0, dtype=torch.float32, device=DEV)
+    out = buf[4096:4096 + n].view(2, 16, 128)
+    shape = gqa.make_shape(2, 16, 4, 1200, 128, gqa.BF16, gqa.BF16, gqa.F32, chunk_tokens=256)
+    ws = torch.zeros(gqa.workspace_bytes(shape) + 8192, dtype=torch.uint8, device=DEV)
+    ws[-8192:] = 0xA5
+    gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"], case["scale"], out=out, chunk_tokens=256,
+               workspace=ws)
+    torch.cuda.synchronize()
+    assert (buf[:4096] == -7.0).all() and (buf[4096 + n:] == -7.0).all()
+    assert (ws[-8192:] == 0xA5).all()
+    assert (ws[: 2 * 4 * 4] == 0).all()      # per-(b, KV head) counters back at zero
+    compare(out, oracle_full(case), "bf16", "guarded")
+
+
+def test_workspace_init_clears_counters():
+    say("workspace init")
+    shape = gqa.make_shape(2, 16, 4, 1200, 128, gqa.BF16, gqa.BF16, chunk_tokens=256)
+    ws = torch.full((gqa.workspace_bytes(shape),), 0x11, dtype=torch.uint8, device=DEV)
+    import ctypes
+    assert gqa.lib.gqa_workspace_init(ws.data_ptr(), ws.numel(), ctypes.byref(shape), None) == 0
+    torch.cuda.synchronize()
+    assert (ws[:32] == 0).all() and (ws[256:512] == 0x11).all()
+
+
+def test_out_of_range_seq_lens_are_clamped_and_reported():
+    say("seq_len clamp")
+    L = 400
+    case = workloads.make_case(3, 8, 2, 128, L, "bf16", "bf16", seq_lens=(L, 10, 5), seed=14)
+    case["seq_lens"] = torch.tensor([L + 50, -3, 5], dtype=torch.int32)
+    d_sl = case["seq_lens"].to(DEV)
+    assert gqa.validate_seq_lens(d_sl, L) == 2
+    got = run(case, out_dtype="f32")
+    case["seq_lens"] = torch.tensor([L, 0, 5], dtype=torch.int32)
+    compare(got, oracle_full(case), "bf16", "clamped")
+    assert (got[1] == 0).all()
+
+
+def test_fp8_descales():
+    say("fp8 descales")
+    case = workloads.make_case(2, 16, 4, 128, 900, "bf16", "fp8_e4m3", seq_lens=(900, 400), seed=15)
+    case["k_descale"], case["v_descale"] = 0.5, 1.75
+    compare(run(case, out_dtype="f32"), oracle_full(case), "fp8_e4m3", "descaled")
+
+
+def test_stream_read_calibration_kernel():
+    say("stream read")
+    src = torch.arange(1 << 20, dtype=torch.int32, device=DEV)
+    sink = gqa.stream_read(src)
+    torch.cuda.synchronize()
+    assert sink.numel() >= 1024
+
+
+# ------------------------------------------------------------------------------ full workloads
+def _sample_rows(case, extra=16, seed=0):
+    B, Hq, G = case["B"], case["Hq"], case["Hq"] // case["Hkv"]
+    sl = case["seq_lens"].tolist()
+    bs = sorted({0, B - 1, int(np.argmin(sl)), int(np.argmax(sl))})
+    hs = sorted({0, G - 1, min(G, Hq - 1), Hq // 2, Hq - 1})
+    rows = {(b, h) for b in bs for h in hs}
+    rng = np.random.default_rng(seed)
+    for _ in range(extra):
+        rows.add((int(rng.integers(B)), int(rng.integers(Hq))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, "4-mha", "4-gqa", "4-mqa", 5])
+def test_workload_parity(wid):
+    """Each named workload at full size, in the launch configuration the benchmark times (library's
+    chunk choice); the oracle checks every row of workload 1 and a sample of rows otherwise."""
+    w = workloads.WORKLOADS[wid]
+    say(f"workload {wid}: {w.name}")
+    case = workloads.make(wid)
+    got = run(case).cpu()
+    if wid == 1:
+        want = oracle_full(case)
+        compare(got, want, w.kv_dtype, f"workload {wid} all rows")
+        return
+    rows = _sample_rows(case)
+    want = ref.decode_rows(case["q"], case["k"], case["v"], case["seq_lens"].numpy(), case["scale"],
+                           rows, case["q_dtype"], case["kv_dtype"], case["k_descale"],
+                           case["v_descale"])
+    sel = torch.stack([got[b, h] for b, h in rows])
+    compare(sel, want, w.kv_dtype, f"workload {wid} {len(rows)} rows")
