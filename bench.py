@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Throughput of single-token GQA decode on one MI355X: KV bytes streamed per second.
+
+A step is one gqa_decode over one batch of the Llama-70B-shaped layer (B32 Hq64 Hkv8 d128 L8192,
+seq_lens ~ U[6000, 8192], bf16) with inputs resident in HBM.  The KV bytes of a step are
+sum_b seq_lens[b] * Hkv * 2 * d * 2 (one K and one V row per cached token and KV head).  Several
+copies of the cache are rotated so that no step finds its cache in the 256 MB last-level cache.
+
+Prints one JSON line on stdout (diagnostics go to stderr).
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV GB/s and % HBM roofline for GQA decode (Hq=64,Hkv=8,d=128,bf16)"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gqa_decode_llama70b_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_attention_04_amd", "csrc", f)
+                  for f in ("gqa_kernels.h", "gqa_api.hip")]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
+    kernel sources as they are now; otherwise None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(case, groups_b):
+    """Time the fp64 oracle (single thread) on every query head of batch entries [0, groups_b)."""
+    from oracle import ref
+
+    rows = [(b, h) for b in range(groups_b) for h in range(case["Hq"])]
+    sl = case["seq_lens"].numpy()
+    t0 = time.perf_counter()
+    ref.decode_rows(case["q"], case["k"], case["v"], sl, case["scale"], rows, case["q_dtype"],
+                    case["kv_dtype"], case["k_descale"], case["v_descale"])
+    dt = time.perf_counter() - t0
+    elt = 1 if case["kv_dtype"] == "fp8_e4m3" else (4 if case["kv_dtype"] == "f32" else 2)
+    kv_bytes = int(sl[:groups_b].sum()) * case["Hkv"] * 2 * case["d"] * elt
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {case['Hq']} query heads of batch entries 0..{groups_b - 1} "
+                      f"({groups_b * case['Hkv']} of {case['B'] * case['Hkv']} (batch, KV head) groups, "
+                      f"{kv_bytes / 1e6:.1f} MB of KV), single-threaded C, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4-mha, 4-gqa, 4-mqa, 5)")
+    ap.add_argument("--copies", type=int, default=0, help="cache copies rotated (0 = enough for 2 GiB)")
+    ap.add_argument("--chunk", type=int, default=0, help="split-K chunk tokens (0 = library choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-batches", type=int, default=16)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain torch copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import grouped_query_attention_04_amd as gqa
+    import workloads
+
+    wid = int(args.workload) if args.workload.isdigit() else args.workload
+    w = workloads.WORKLOADS[wid]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"workload {wid}: {w.name}; generating inputs")
+    case = workloads.make(wid)
+    elt = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
+    sl = case["seq_lens"]
+    kv_bytes = int(sl.sum()) * w.Hkv * 2 * w.d * elt
+    alloc = 2 * case["k"].numel() * elt
+    copies = args.copies or max(2, -(-(2 << 30) // alloc))
+
+    q = case["q"].to(dev)
+    seq = sl.to(dev)
+    ks = [case["k"].to(dev) for _ in range(copies)]
+    vs = [case["v"].to(dev) for _ in range(copies)]
+    od = workloads.TORCH_DTYPES[w.out_dtype]
+    out = torch.empty(w.B, w.Hq, w.d, dtype=od, device=dev)
+    code = {"f32": gqa.F32, "bf16": gqa.BF16, "fp8_e4m3": gqa.FP8_E4M3}
+    shape = gqa.make_shape(w.B, w.Hq, w.Hkv, w.L, w.d, code[w.q_dtype], code[w.kv_dtype],
+                           code[w.out_dtype], chunk_tokens=args.chunk)
+    ws = torch.zeros(gqa.workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    shape_ref = ctypes.byref(shape)
+    kptr = [t.data_ptr() for t in ks]
+    vptr = [t.data_ptr() for t in vs]
+    scale = float(case["scale"])
+
+    def step(i):
+        rc = gqa.lib.gqa_decode(q.data_ptr(), kptr[i % copies], vptr[i % copies], seq.data_ptr(), scale,
+                                out.data_ptr(), shape_ref, ws.data_ptr(), ws.numel(), sh)
+        if rc:
+            raise RuntimeError(gqa.status_string(rc))
+
+    log(f"{copies} cache copies of {alloc / 2**20:.0f} MiB; KV bytes per step {kv_bytes / 1e6:.1f} MB; "
+        f"chunk {args.chunk or 'auto'}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps between two device synchronisations; per-launch HIP events on the
+    # launch stream give the kernel's average duration for the roofline figure
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    launch_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = kv_bytes / (avg_launch_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us wall; kernel avg {avg_launch_ms * 1e3:.1f} us "
+        f"(p10 {launch_ms[len(launch_ms) // 10] * 1e3:.1f}, p90 {launch_ms[9 * len(launch_ms) // 10] * 1e3:.1f}); "
+        f"{achieved:.0f} GB/s = {100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+
+    # achievable streaming-read bandwidth on one cache copy, for context
+    sink = torch.empty(gqa.lib.gqa_stream_read_sink_words(), dtype=torch.int32, device=dev)
+    for i in range(3):
+        gqa.stream_read(ks[i % copies], sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(10):
+        gqa.stream_read(ks[i % copies], sink)
+        gqa.stream_read(vs[i % copies], sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    calib = 20 * ks[0].numel() * elt / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    log(f"calibration: non-temporal streaming read of the cache copies {calib:.0f} GB/s")
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calib_copy_mib} MiB done")
+
+    traffic = recorded_traffic()
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.kv_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L,
+                   "seq_lens": f"sum {int(sl.sum())} (min {int(sl.min())}, max {int(sl.max())})",
+                   "kv_bytes_per_step": kv_bytes, "cache_copies": copies,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the same workload")
+        result["cpu_baseline"] = cpu_baseline(case, min(args.cpu_sample_batches, w.B))
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

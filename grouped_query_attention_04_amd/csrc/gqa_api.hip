@@ -24,14 +24,23 @@ bool known_dtype(int dt) { return dt == GQA_F32 || dt == GQA_BF16 || dt == GQA_F
 // Split-K chunk length: the largest multiple of 256 tokens that still yields about
 // kTargetWorkgroups (batch, KV head, chunk) work items, so that every CU gets several and the
 // per-chunk partial results stay a small fraction of the cache bytes.
+// The chunk count per sequence is also bounded so that the final merge can stage every chunk's
+// (max, sum) for the G query rows in LDS.
+long long min_chunk(const gqa_shape_t* s) {
+  const long long G = s->Hq / s->Hkv;
+  const long long need = ((long long)s->L * G + gqa::kCombinePairs - 1) / gqa::kCombinePairs;
+  return (need + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+}
+
 int plan_chunk(const gqa_shape_t* s) {
   if (s->chunk_tokens > 0) return s->chunk_tokens;
   const long long units = (long long)s->B * s->Hkv;
-  for (int c = 4096; c > kChunkQuantum; c /= 2) {
+  const long long lo = min_chunk(s) > kChunkQuantum ? min_chunk(s) : kChunkQuantum;
+  for (long long c = 4096; c > lo; c /= 2) {
     const long long nc = (s->L + c - 1) / c;
-    if (units * nc >= kTargetWorkgroups) return c;
+    if (units * nc >= kTargetWorkgroups) return (int)c;
   }
-  return kChunkQuantum;
+  return (int)(lo > 4096 ? lo : (lo > kChunkQuantum ? lo : kChunkQuantum));
 }
 
 struct Layout {
@@ -108,6 +117,7 @@ gqa_status_t gqa_shape_check(const gqa_shape_t* s) {
   if (!f32_path && !mfma_path) return GQA_ERR_UNSUPPORTED;
   // per-(batch, KV head) cache slices are addressed with 32-bit byte offsets
   if ((long long)s->L * s->d * elt_bytes(s->kv_dtype) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
+  if (s->chunk_tokens > 0 && s->chunk_tokens < min_chunk(s)) return GQA_ERR_UNSUPPORTED;
   const long long c = plan_chunk(s);
   if ((long long)s->B * s->Hkv * ((s->L + c - 1) / c) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
   if ((long long)s->B * s->Hq >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;

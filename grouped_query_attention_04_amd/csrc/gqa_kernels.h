@@ -113,80 +113,135 @@ struct EpiLayout {
   static constexpr int kBytes = NW * GT * (2 + kRow) * 4;
 };
 
+// The last workgroup of a (b, j) stages every chunk's (max, sum) in LDS; the host keeps
+// nchunks * G within this many pairs.
+constexpr int kCombinePairs = 2048;
+constexpr int kCombineBytes = kCombinePairs * 8 + 32 * 4;
+
+// Workspace traffic between workgroups uses agent-scope cache policy (sc1): the bits the compiler
+// gives agent-scope atomic loads and stores, which keep them coherent across the per-XCD L2
+// caches without a whole-cache write-back or invalidate.
+constexpr int kAgentScope = 16;
+
+__device__ __forceinline__ void store4_agent(float* base, uint32_t bytes, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), make_rsrc(base, bytes), off, 0, kAgentScope);
+}
+
 template <int GT, int D, int NW, typename OutT>
 __device__ void epilogue(const Params& p, float* ep, int b, int j, int c, int nlive) {
+  constexpr int NTH = NW * 64;
+  constexpr int kRow = EpiLayout<GT, D, NW>::kRow;
   const int tid = threadIdx.x;
   const int G = p.G;
   const int bj = b * p.Hkv + j;
-  float* ep_m = ep;
-  float* ep_l = ep + NW * GT;
-  float* ep_o = ep + 2 * NW * GT;
-  constexpr int kRow = EpiLayout<GT, D, NW>::kRow;
+  const float* ep_m = ep;
+  const float* ep_l = ep + NW * GT;
+  const float* ep_o = ep + 2 * NW * GT;
   OutT* out = reinterpret_cast<OutT*>(p.out) + ((size_t)b * p.Hq + (size_t)j * G) * D;
 
+  // merge of the NW wave states for 4 consecutive columns of one query row
+  auto merge4 = [&](int item, float& M, float& l, f32x4_t& o) {
+    const int g = (4 * item) / D, cc = (4 * item) % D;
+    M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, ep_m[w * GT + g]);
+    l = 0.f;
+    o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float s = __builtin_amdgcn_exp2f(ep_m[w * GT + g] - M);
+      l += s * ep_l[w * GT + g];
+      o += s * *reinterpret_cast<const f32x4_t*>(ep_o + (w * GT + g) * kRow + cc);
+    }
+  };
+
   if (nlive == 1) {  // the whole sequence was in this chunk: normalise and store
-    for (int idx = tid; idx < G * D; idx += NW * 64) {
-      const int g = idx / D, cc = idx % D;
-      float M = -INFINITY;
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, ep_m[w * GT + g]);
-      float l = 0.f, o = 0.f;
-      for (int w = 0; w < NW; ++w) {
-        const float s = __builtin_amdgcn_exp2f(ep_m[w * GT + g] - M);
-        l += s * ep_l[w * GT + g];
-        o += s * ep_o[(w * GT + g) * kRow + cc];
-      }
-      store_out(out + (size_t)g * D + cc, o / l * p.v_descale);
+    for (int item = tid; item < G * D / 4; item += NTH) {
+      float M, l;
+      f32x4_t o;
+      merge4(item, M, l, o);
+      const float inv = p.v_descale / l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out(out + 4 * item + e, o[e] * inv);
     }
     return;
   }
 
-  // Several chunks: publish this chunk's partial result.
+  // Several chunks: publish this chunk's partial result with agent-scope stores.
   float* po = p.part_o + ((size_t)bj * p.nchunks + c) * G * D;
   float* pml = p.part_ml + ((size_t)bj * p.nchunks + c) * G * 2;
-  for (int idx = tid; idx < G * D; idx += NW * 64) {
-    const int g = idx / D, cc = idx % D;
-    float M = -INFINITY;
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, ep_m[w * GT + g]);
-    float l = 0.f, o = 0.f;
-    for (int w = 0; w < NW; ++w) {
-      const float s = __builtin_amdgcn_exp2f(ep_m[w * GT + g] - M);
-      l += s * ep_l[w * GT + g];
-      o += s * ep_o[(w * GT + g) * kRow + cc];
-    }
-    po[idx] = o;
-    if (cc == 0) {
-      pml[2 * g] = M;
-      pml[2 * g + 1] = l;
+  for (int item = tid; item < G * D / 4; item += NTH) {
+    float M, l;
+    f32x4_t o;
+    merge4(item, M, l, o);
+    store4_agent(po, G * D * 4, item * 16, o);
+    if ((4 * item) % D == 0) {
+      const int g = (4 * item) / D;
+      __hip_atomic_store(pml + 2 * g, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pml + 2 * g + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  // Make this workgroup's partial visible device-wide, then count the chunk as finished.
-  __threadfence();
+  // Every store of this thread has completed at agent scope before the barrier; after it, one
+  // thread counts the chunk as finished.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   __shared__ int s_last;
   if (tid == 0) {
-    const uint32_t done = atomicAdd(p.counters + bj, 1u);
+    const uint32_t done = __hip_atomic_fetch_add(p.counters + bj, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (done == (uint32_t)(nlive - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  // Acquire at agent scope: drop this XCD's cached copies of the workspace lines, so the loads
+  // below see what the other workgroups wrote through to memory.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  // Last chunk of (b, j): log-sum-exp merge of all nlive partials, in chunk order.
-  const float* po0 = p.part_o + (size_t)bj * p.nchunks * G * D;
+  // Last chunk of (b, j) to finish: log-sum-exp merge of all nlive partials, in chunk order.
+  float* cm = ep;                        // [nlive][G] chunk max, then its weight
+  float* cl = ep + kCombinePairs;        // [nlive][G] chunk sum
+  float* cinv = ep + 2 * kCombinePairs;  // [G] v_descale / total sum
   const float* pml0 = p.part_ml + (size_t)bj * p.nchunks * G * 2;
-  for (int idx = tid; idx < G * D; idx += NW * 64) {
-    const int g = idx / D;
+  const float* po0 = p.part_o + (size_t)bj * p.nchunks * G * D;
+  const uint32_t o_bytes = (uint32_t)(nlive * G * D * 4);
+  for (int i = tid; i < nlive * G; i += NTH) {
+    cm[i] = __hip_atomic_load(pml0 + 2 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    cl[i] = __hip_atomic_load(pml0 + 2 * i + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  for (int g = tid; g < G; g += NTH) {
     float M = -INFINITY;
-    for (int k = 0; k < nlive; ++k) M = fmaxf(M, __builtin_nontemporal_load(pml0 + (size_t)k * G * 2 + 2 * g));
-    float l = 0.f, o = 0.f;
+    for (int k = 0; k < nlive; ++k) M = fmaxf(M, cm[k * G + g]);
+    float l = 0.f;
     for (int k = 0; k < nlive; ++k) {
-      const float mk = __builtin_nontemporal_load(pml0 + (size_t)k * G * 2 + 2 * g);
-      const float lk = __builtin_nontemporal_load(pml0 + (size_t)k * G * 2 + 2 * g + 1);
-      const float s = __builtin_amdgcn_exp2f(mk - M);
-      l += s * lk;
-      o += s * __builtin_nontemporal_load(po0 + (size_t)k * G * D + idx);
+      const float s = __builtin_amdgcn_exp2f(cm[k * G + g] - M);
+      cm[k * G + g] = s;
+      l += s * cl[k * G + g];
     }
-    store_out(out + idx, o / l * p.v_descale);
+    cinv[g] = p.v_descale / l;
+  }
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(po0, o_bytes);
+  for (int item = tid; item < G * D / 4; item += NTH) {
+    const int g = (4 * item) / D;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    int k = 0;
+    for (; k + 4 <= nlive; k += 4) {  // four partial loads in flight per thread
+      u32x4_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, ((k + u) * G * D + 4 * item) * 4, 0, kAgentScope));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += cm[(k + u) * G + g] * __builtin_bit_cast(f32x4_t, v[u]);
+    }
+    for (; k < nlive; ++k) {
+      const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, (k * G * D + 4 * item) * 4, 0, kAgentScope));
+      acc += cm[k * G + g] * __builtin_bit_cast(f32x4_t, v);
+    }
+    const float inv = cinv[g];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(out + 4 * item + e, acc[e] * inv);
   }
   if (tid == 0) __hip_atomic_store(p.counters + bj, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -228,7 +283,7 @@ __device__ __forceinline__ bool decode_work_item(const Params& p, int& b, int& j
 //   so the running max / sum of row g live in the same lanes as its outputs.
 // NT = 16-row tiles of query rows (G <= 16 * NT).
 template <int D, int NT, bool FP8, typename OutT, int NW>
-__global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(Params p) {
+__global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(Params p) {
   constexpr int TILE = 32;
   constexpr int KS = D / 32;          // k-steps of QK^T
   constexpr int MT = D / 16;          // m-tiles of PV
@@ -240,7 +295,8 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(Params p) {
   constexpr int VTILE = TILE * D * 2;            // bytes of one LDS V tile (bf16)
   constexpr int GT = 16 * NT;
   using Epi = EpiLayout<GT, D, NW>;
-  constexpr int SMEM = (NW * VTILE > Epi::kBytes) ? NW * VTILE : Epi::kBytes;
+  constexpr int SMEM0 = (NW * VTILE > Epi::kBytes) ? NW * VTILE : Epi::kBytes;
+  constexpr int SMEM = SMEM0 > kCombineBytes ? SMEM0 : kCombineBytes;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   int b, j, c, n, nlive;
@@ -463,7 +519,8 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
   constexpr int QB = GT * D * 4;
   constexpr int PB = NW * GT * TILE * 4;
   constexpr int MAIN = QB + PB;
-  constexpr int SMEM = MAIN > Epi::kBytes ? MAIN : Epi::kBytes;
+  constexpr int SMEM0 = MAIN > Epi::kBytes ? MAIN : Epi::kBytes;
+  constexpr int SMEM = SMEM0 > kCombineBytes ? SMEM0 : kCombineBytes;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
   int b, j, c, n, nlive;
