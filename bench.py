@@ -77,7 +77,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4-mha, 4-gqa, 4-mqa, 5)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated (0 = enough for 2 GiB)")
-    ap.add_argument("--chunk", type=int, default=0, help="split-K chunk tokens (0 = library choice)")
+    ap.add_argument("--workgroups", type=int, default=0, help="workgroups (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=16)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -115,7 +115,7 @@ def main():
     out = torch.empty(w.B, w.Hq, w.d, dtype=od, device=dev)
     code = {"f32": gqa.F32, "bf16": gqa.BF16, "fp8_e4m3": gqa.FP8_E4M3}
     shape = gqa.make_shape(w.B, w.Hq, w.Hkv, w.L, w.d, code[w.q_dtype], code[w.kv_dtype],
-                           code[w.out_dtype], chunk_tokens=args.chunk)
+                           code[w.out_dtype], num_workgroups=args.workgroups)
     ws = torch.zeros(gqa.workspace_bytes(shape), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
@@ -131,7 +131,7 @@ def main():
             raise RuntimeError(gqa.status_string(rc))
 
     log(f"{copies} cache copies of {alloc / 2**20:.0f} MiB; KV bytes per step {kv_bytes / 1e6:.1f} MB; "
-        f"chunk {args.chunk or 'auto'}")
+        f"workgroups {args.workgroups or 'auto'}")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -36,7 +36,7 @@ class Shape(ctypes.Structure):
                 ("L", ctypes.c_int32), ("d", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("kv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
-                ("chunk_tokens", ctypes.c_int32)]
+                ("num_workgroups", ctypes.c_int32)]
 
 
 EXPORTS = ["gqa_shape_check", "gqa_decode_workspace_bytes", "gqa_workspace_init", "gqa_decode",
@@ -84,9 +84,9 @@ def status_string(code: int) -> str:
 
 
 def make_shape(B, Hq, Hkv, L, d, q_dtype=BF16, kv_dtype=BF16, out_dtype=None, k_descale=1.0,
-               v_descale=1.0, chunk_tokens=0) -> Shape:
+               v_descale=1.0, num_workgroups=0) -> Shape:
     return Shape(B, Hq, Hkv, L, d, q_dtype, kv_dtype, q_dtype if out_dtype is None else out_dtype,
-                 k_descale, v_descale, chunk_tokens)
+                 k_descale, v_descale, num_workgroups)
 
 
 def shape_check(shape: Shape) -> int:
@@ -109,8 +109,9 @@ _workspaces = {}
 
 
 def workspace_for(shape: Shape, device) -> torch.Tensor:
-    """A zero-initialised workspace cached per (device, stream, size).  Calls that overlap in time
-    on different streams get different buffers; calls on one stream share it."""
+    """A workspace cached per (device, stream), zeroed when allocated and grown when a shape needs
+    more.  The library leaves its counters at zero after every call, so one buffer serves every
+    shape.  Calls that overlap in time on different streams get different buffers."""
     need = workspace_bytes(shape)
     if need == 0:
         _check(shape_check(shape))
@@ -123,20 +124,21 @@ def workspace_for(shape: Shape, device) -> torch.Tensor:
     return ws
 
 
-def _shape_from(q, k_cache, out_dtype, k_descale, v_descale, chunk_tokens):
+def _shape_from(q, k_cache, out_dtype, k_descale, v_descale, num_workgroups):
     B, Hq, d = q.shape
     _, Hkv, L, _ = k_cache.shape
     if q.dtype not in _CODE or k_cache.dtype not in _CODE or out_dtype not in _CODE:
         raise TypeError(f"unsupported dtypes q={q.dtype} kv={k_cache.dtype} out={out_dtype}")
     return make_shape(B, Hq, Hkv, L, d, _CODE[q.dtype], _CODE[k_cache.dtype], _CODE[out_dtype],
-                      k_descale, v_descale, chunk_tokens)
+                      k_descale, v_descale, num_workgroups)
 
 
 def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, *, out_dtype=None, k_descale=1.0,
-           v_descale=1.0, chunk_tokens=0, workspace=None):
+           v_descale=1.0, num_workgroups=0, workspace=None):
     """Single-token GQA decode.  q [B,Hq,d]; k_cache, v_cache [B,Hkv,L,d]; seq_lens [B] int32;
     all contiguous CUDA tensors on one device.  Returns out [B,Hq,d] (dtype out_dtype, default q's).
-    scale defaults to 1/sqrt(d).  Enqueued on torch's current stream; no synchronisation."""
+    scale defaults to 1/sqrt(d).  num_workgroups (0 = library's choice) sets how many workgroups
+    split the cache.  Enqueued on torch's current stream; no synchronisation."""
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("expected q [B,Hq,d], k_cache and v_cache [B,Hkv,L,d]")
     if k_cache.dtype != v_cache.dtype:
@@ -160,7 +162,7 @@ def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, *, out_dtype=Non
         raise ValueError("out must be [B,Hq,d] of dtype out_dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    shape = _shape_from(q, k_cache, out_dtype, k_descale, v_descale, chunk_tokens)
+    shape = _shape_from(q, k_cache, out_dtype, k_descale, v_descale, num_workgroups)
     ws = workspace if workspace is not None else workspace_for(shape, dev)
     with torch.cuda.device(dev):
         _check(lib.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),

@@ -11,9 +11,9 @@
 
 namespace {
 
-constexpr int kWaves = 4;             // waves per workgroup
-constexpr int kChunkQuantum = 256;    // chunk lengths are multiples of this many tokens
-constexpr int kTargetWorkgroups = 2048;  // 8 per compute unit on a 256-CU MI355X
+constexpr int kWaves = 4;              // waves per workgroup
+constexpr int kDefaultWorkgroups = 256;  // one per compute unit of an MI355X
+constexpr int kMaxWorkgroups = 65536;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -21,43 +21,30 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int elt_bytes(int dt) { return dt == GQA_F32 ? 4 : dt == GQA_BF16 ? 2 : 1; }
 bool known_dtype(int dt) { return dt == GQA_F32 || dt == GQA_BF16 || dt == GQA_FP8_E4M3; }
 
-// Split-K chunk length: the largest multiple of 256 tokens that still yields about
-// kTargetWorkgroups (batch, KV head, chunk) work items, so that every CU gets several and the
-// per-chunk partial results stay a small fraction of the cache bytes.
-// The chunk count per sequence is also bounded so that the final merge can stage every chunk's
-// (max, sum) for the G query rows in LDS.
-long long min_chunk(const gqa_shape_t* s) {
-  const long long G = s->Hq / s->Hkv;
-  const long long need = ((long long)s->L * G + gqa::kCombinePairs - 1) / gqa::kCombinePairs;
-  return (need + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+int plan_workgroups(const gqa_shape_t* s) {
+  return s->num_workgroups > 0 ? s->num_workgroups : kDefaultWorkgroups;
 }
 
-int plan_chunk(const gqa_shape_t* s) {
-  if (s->chunk_tokens > 0) return s->chunk_tokens;
-  const long long units = (long long)s->B * s->Hkv;
-  const long long lo = min_chunk(s) > kChunkQuantum ? min_chunk(s) : kChunkQuantum;
-  for (long long c = 4096; c > lo; c /= 2) {
-    const long long nc = (s->L + c - 1) / c;
-    if (units * nc >= kTargetWorkgroups) return (int)c;
-  }
-  return (int)(lo > 4096 ? lo : (lo > kChunkQuantum ? lo : kChunkQuantum));
-}
+// Workspace: a counter area of fixed size (one counter per (batch, KV head), for up to kMaxUnits
+// of them), then two published-piece slots per workgroup.  Because the counter area never moves,
+// no shape's partial results ever land on another shape's counters, and since every call leaves its
+// counters at zero, a workspace zeroed once can serve calls of any shape.
+constexpr size_t kMaxUnits = size_t(1) << 18;
 
 struct Layout {
-  int chunk, nchunks;
+  int workgroups;
   size_t counters_off, ml_off, o_off, total;
 };
 
 Layout plan(const gqa_shape_t* s) {
   Layout lo;
-  lo.chunk = plan_chunk(s);
-  lo.nchunks = (s->L + lo.chunk - 1) / lo.chunk;
-  const size_t units = (size_t)s->B * s->Hkv;
+  lo.workgroups = plan_workgroups(s);
+  const size_t slots = (size_t)lo.workgroups * 2;
   const size_t G = (size_t)(s->Hq / s->Hkv);
   lo.counters_off = 0;
-  lo.ml_off = align_up(units * sizeof(uint32_t));
-  lo.o_off = lo.ml_off + align_up(units * lo.nchunks * G * 2 * sizeof(float));
-  lo.total = lo.o_off + align_up(units * lo.nchunks * G * (size_t)s->d * sizeof(float));
+  lo.ml_off = kMaxUnits * sizeof(uint32_t);
+  lo.o_off = lo.ml_off + align_up(slots * G * 2 * sizeof(float));
+  lo.total = lo.o_off + align_up(slots * G * (size_t)s->d * sizeof(float));
   return lo;
 }
 
@@ -108,7 +95,7 @@ gqa_status_t gqa_shape_check(const gqa_shape_t* s) {
   if (!known_dtype(s->q_dtype) || !known_dtype(s->kv_dtype) || !known_dtype(s->out_dtype))
     return GQA_ERR_INVALID_ARG;
   if (!std::isfinite(s->k_descale) || !std::isfinite(s->v_descale)) return GQA_ERR_INVALID_ARG;
-  if (s->chunk_tokens < 0 || s->chunk_tokens % kChunkQuantum != 0) return GQA_ERR_INVALID_ARG;
+  if (s->num_workgroups < 0 || s->num_workgroups > kMaxWorkgroups) return GQA_ERR_INVALID_ARG;
   if (s->d != 64 && s->d != 128) return GQA_ERR_UNSUPPORTED;
   if (s->Hq / s->Hkv > 32) return GQA_ERR_UNSUPPORTED;
   if (s->out_dtype != GQA_F32 && s->out_dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
@@ -117,10 +104,10 @@ gqa_status_t gqa_shape_check(const gqa_shape_t* s) {
   if (!f32_path && !mfma_path) return GQA_ERR_UNSUPPORTED;
   // per-(batch, KV head) cache slices are addressed with 32-bit byte offsets
   if ((long long)s->L * s->d * elt_bytes(s->kv_dtype) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
-  if (s->chunk_tokens > 0 && s->chunk_tokens < min_chunk(s)) return GQA_ERR_UNSUPPORTED;
-  const long long c = plan_chunk(s);
-  if ((long long)s->B * s->Hkv * ((s->L + c - 1) / c) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
+  // the tile space (tiles of 32 positions per batch entry and KV head) is indexed with 32-bit ints
+  if ((long long)s->B * s->Hkv * ((s->L + 31) / 32) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
   if ((long long)s->B * s->Hq >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
+  if ((size_t)s->B * s->Hkv > kMaxUnits) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
 }
 
@@ -171,12 +158,11 @@ gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
   prm.Hkv = s->Hkv;
   prm.L = s->L;
   prm.G = s->Hq / s->Hkv;
-  prm.chunk = lo.chunk;
-  prm.nchunks = lo.nchunks;
+  prm.W = lo.workgroups;
   prm.qk_scale = (float)((double)scale * (double)s->k_descale * 1.4426950408889634);
   prm.v_descale = s->v_descale;
 
-  const int grid = s->B * s->Hkv * lo.nchunks;
+  const int grid = lo.workgroups;
   hipStream_t hs = (hipStream_t)stream;
   if (s->kv_dtype == GQA_F32) {
     return s->d == 64 ? dispatch_f32<64>(prm.G, s->out_dtype, grid, prm, hs)
@@ -220,7 +206,7 @@ gqa_status_t gqa_stream_read(const void* src, size_t bytes, void* sink, void* st
 const char* gqa_status_string(gqa_status_t status) {
   switch (status) {
     case GQA_OK: return "GQA_OK: success";
-    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG: null or misaligned pointer, bad dimension, Hq not a multiple of Hkv, bad chunk length or size overflow";
+    case GQA_ERR_INVALID_ARG: return "GQA_ERR_INVALID_ARG: null or misaligned pointer, bad dimension, Hq not a multiple of Hkv, bad workgroup count or size overflow";
     case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: head dim, group size, dtype combination or size outside what the library implements";
     case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or smaller than gqa_decode_workspace_bytes()";
     case GQA_ERR_HIP: return "GQA_ERR_HIP: the HIP runtime reported an error while enqueueing";

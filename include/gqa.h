@@ -61,21 +61,24 @@ typedef struct {
   int32_t B, Hq, Hkv, L, d;
   int32_t q_dtype, kv_dtype, out_dtype; /* gqa_dtype_t values */
   float k_descale, v_descale;           /* 1.0 for f32 and bf16 caches */
-  int32_t chunk_tokens; /* split-K chunk length in tokens: 0 = library's choice, else a positive
-                           multiple of 256 */
+  int32_t num_workgroups; /* workgroups that split the cache: 0 = library's choice (256), else
+                             1..65536.  Results do not depend on it beyond rounding. */
 } gqa_shape_t;
 
-/* Validates a shape (dimensions, divisibility, dtypes, chunk length, 32-bit per-head offsets).
+/* Validates a shape (dimensions, divisibility, dtypes, workgroup count, 32-bit offsets).
  * Host only; no HIP call.  Returns GQA_OK, GQA_ERR_INVALID_ARG or GQA_ERR_UNSUPPORTED. */
 gqa_status_t gqa_shape_check(const gqa_shape_t* shape);
 
-/* Bytes of device workspace gqa_decode needs for this shape (split-K partial results and one
- * counter per (batch, KV head)); 0 if the shape is invalid.  Host only. */
+/* Bytes of device workspace gqa_decode needs for this shape: a fixed 1 MiB area of counters (one
+ * per (batch, KV head); B * Hkv may not exceed 2^18) followed by two partial-result slots per
+ * workgroup.  0 if the shape is invalid.  Host only. */
 size_t gqa_decode_workspace_bytes(const gqa_shape_t* shape);
 
-/* Clears the counter part of a workspace.  A workspace must have been cleared once (by this call or
- * by zero-filling it) before its first gqa_decode; every gqa_decode that completes leaves the
- * counters at zero again.  Enqueues one small kernel on `stream` (a hipStream_t, NULL = default). */
+/* Clears the counter area of a workspace.  A workspace must be cleared once (by this call or by
+ * zero-filling it) before its first gqa_decode; every gqa_decode that completes leaves the counters
+ * at zero again, so the workspace then serves later calls of any shape that fits in it.  Writing
+ * anything else into the counter area requires clearing it again.  Enqueues one small kernel on
+ * `stream` (a hipStream_t, NULL = the default stream). */
 gqa_status_t gqa_workspace_init(void* workspace, size_t workspace_bytes, const gqa_shape_t* shape,
                                 void* stream);
 

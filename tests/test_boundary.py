@@ -48,14 +48,14 @@ def test_valid_shapes_pass():
     assert gqa.shape_check(_shape(d=128, q_dtype=gqa.BF16, kv_dtype=gqa.BF16)) == 0
     assert gqa.shape_check(_shape(d=128, q_dtype=gqa.BF16, kv_dtype=gqa.FP8_E4M3, out_dtype=gqa.F32)) == 0
     assert gqa.shape_check(_shape(Hq=32, Hkv=1, q_dtype=gqa.BF16, kv_dtype=gqa.BF16)) == 0
-    assert gqa.shape_check(_shape(Hq=6, Hkv=2, chunk_tokens=512)) == 0
+    assert gqa.shape_check(_shape(Hq=6, Hkv=2, num_workgroups=7)) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(Hq=6, Hkv=4), 1),                 # Hq not a multiple of Hkv
     (dict(B=0), 1), (dict(Hkv=0), 1), (dict(L=0), 1), (dict(d=-64), 1),
     (dict(q_dtype=7), 1),                   # unknown dtype code
-    (dict(chunk_tokens=100), 1), (dict(chunk_tokens=-256), 1),
+    (dict(num_workgroups=-1), 1), (dict(num_workgroups=70000), 1),
     (dict(d=96), 2), (dict(d=256), 2),      # head dims outside {64, 128}
     (dict(Hq=66, Hkv=1), 2),                # group larger than 32
     (dict(q_dtype=gqa.F32, kv_dtype=gqa.BF16), 2),
@@ -63,6 +63,7 @@ def test_valid_shapes_pass():
     (dict(q_dtype=gqa.FP8_E4M3, kv_dtype=gqa.FP8_E4M3), 2),
     (dict(out_dtype=gqa.FP8_E4M3), 2),
     (dict(L=1 << 22, d=128), 2),            # per-head slice beyond 32-bit byte offsets
+    (dict(B=1 << 17, Hq=8, Hkv=4), 2),      # more (batch, KV head) pairs than counters
 ])
 def test_bad_shapes_rejected(kw, code):
     assert gqa.shape_check(_shape(**kw)) == code
@@ -74,14 +75,15 @@ def test_nonfinite_descale_rejected():
     assert gqa.shape_check(_shape(v_descale=float("nan"))) == 1
 
 
-def test_workspace_grows_with_chunks_and_is_aligned():
-    a = gqa.workspace_bytes(_shape(L=4096, chunk_tokens=1024))
-    b = gqa.workspace_bytes(_shape(L=4096, chunk_tokens=256))
+def test_workspace_grows_with_workgroups_and_is_aligned():
+    a = gqa.workspace_bytes(_shape(L=4096, num_workgroups=64))
+    b = gqa.workspace_bytes(_shape(L=4096, num_workgroups=256))
     assert a > 0 and b > a and a % 256 == 0 and b % 256 == 0
-    # counters (B*Hkv u32) + (m, l) and d floats per (unit, chunk, query row)
-    s = _shape(L=4096, chunk_tokens=256)
-    units, nch, G, d = 4, 16, 4, 64
-    assert b >= units * 4 + units * nch * G * (2 + d) * 4
+    # fixed counter area + two slots per workgroup of (m, l) and d floats per query row
+    slots, G, d = 512, 4, 64
+    assert b >= (1 << 20) + slots * G * (2 + d) * 4
+    assert b - a == 2 * (256 - 64) * G * (2 + d) * 4
+    assert gqa.workspace_bytes(_shape(L=4096)) == gqa.workspace_bytes(_shape(L=4096, num_workgroups=256))
 
 
 def test_decode_rejects_before_any_hip_call():

@@ -32,13 +32,13 @@ def to_dev(case):
     return {k: (v.to(DEV) if torch.is_tensor(v) else v) for k, v in case.items()}
 
 
-def run(case, out_dtype=None, chunk_tokens=0, scale=None):
+def run(case, out_dtype=None, workgroups=0, scale=None):
     d = to_dev(case)
     od = TORCH[out_dtype or case["out_dtype"]]
     out = gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"],
                      case["scale"] if scale is None else scale, out_dtype=od,
                      k_descale=case["k_descale"], v_descale=case["v_descale"],
-                     chunk_tokens=chunk_tokens)
+                     num_workgroups=workgroups)
     torch.cuda.synchronize()
     return out
 
@@ -92,7 +92,7 @@ def test_worked_example_2_on_gpu(qd, kd):
 
 # ------------------------------------------------------------------------------ small shapes
 SMALL = [
-    # (B, Hq, Hkv, d, L, seq_lens, chunk)
+    # (B, Hq, Hkv, d, L, seq_lens, workgroups)
     (3, 16, 4, 128, 1100, (1100, 777, 33), 256),
     (2, 8, 2, 64, 700, (700, 1), 256),
     (2, 8, 8, 128, 600, (513, 600), 256),      # G = 1 (MHA)
@@ -107,12 +107,12 @@ SMALL = [
 @pytest.mark.parametrize("qd,kd", DTYPES)
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}d{c[3]}L{c[4]}")
 def test_small_parity(cfg, qd, kd):
-    B, Hq, Hkv, d, L, sl, chunk = cfg
+    B, Hq, Hkv, d, L, sl, wg = cfg
     say(f"small parity {cfg} q={qd} kv={kd}")
     case = workloads.make_case(B, Hq, Hkv, d, L, qd, kd, seq_lens=sl, seed=hash(cfg) % 10000)
     want = oracle_full(case)
-    compare(run(case, chunk_tokens=chunk), want, kd, "native out")
-    compare(run(case, out_dtype="f32", chunk_tokens=chunk), want, kd, "f32 out")
+    compare(run(case, workgroups=wg), want, kd, "native out")
+    compare(run(case, out_dtype="f32", workgroups=wg), want, kd, "f32 out")
 
 
 # ------------------------------------------------------------------------------ edge cases
@@ -123,7 +123,7 @@ def test_seq_len_edges(qd, kd):
     say(f"seq_len edges {sl} q={qd} kv={kd}")
     case = workloads.make_case(len(sl), 16, 4, 128, L, qd, kd, seq_lens=sl, seed=77)
     want = oracle_full(case)
-    got = run(case, out_dtype="f32", chunk_tokens=256)
+    got = run(case, out_dtype="f32", workgroups=13)
     assert (got[0] == 0).all()
     compare(got, want, kd, "edges")
 
@@ -133,7 +133,7 @@ def test_padding_is_never_read(qd, kd):
     say(f"NaN-poisoned padding q={qd} kv={kd}")
     sl = (300, 33, 1)
     case = workloads.make_case(3, 8, 2, 128, 512, qd, kd, seq_lens=sl, seed=5)
-    base = run(case, out_dtype="f32", chunk_tokens=256).clone()
+    base = run(case, out_dtype="f32", workgroups=13).clone()
     for key in ("k", "v"):
         t = case[key]
         raw = t.view(torch.uint8) if kd == "fp8_e4m3" else t
@@ -142,7 +142,7 @@ def test_padding_is_never_read(qd, kd):
                 raw[b, :, n:] = 0x7F        # e4m3fn NaN code
             else:
                 raw[b, :, n:] = float("nan")
-    got = run(case, out_dtype="f32", chunk_tokens=256)
+    got = run(case, out_dtype="f32", workgroups=13)
     assert torch.isfinite(got).all()
     assert torch.equal(got, base)
 
@@ -157,7 +157,7 @@ def test_constant_v_per_kv_head():
         for j in range(Hkv):
             v[b, j] = j + 10 * b
     case["v"] = v.to(torch.bfloat16)
-    got = run(case, out_dtype="f32", chunk_tokens=256).cpu().double()
+    got = run(case, out_dtype="f32", workgroups=13).cpu().double()
     G = Hq // Hkv
     want = torch.tensor([[h // G + 10 * b for h in range(Hq)] for b in range(B)], dtype=torch.float64)
     assert torch.allclose(got, want[:, :, None].expand_as(got), rtol=2e-6, atol=0)
@@ -174,7 +174,7 @@ def test_zero_query_gives_prefix_mean(qd, kd):
     if kd != "f32":        # keep the values exact in bf16 and e4m3 (integers below 16)
         t = t % 16
     case["v"] = workloads.cast(t[None, None, :, None].expand(B, Hkv, L, d).contiguous(), kd)
-    got = run(case, out_dtype="f32", chunk_tokens=256).cpu().double()
+    got = run(case, out_dtype="f32", workgroups=13).cpu().double()
     compare(got, oracle_full(case), kd, "zero q")
     if kd == "f32":
         for b, n in enumerate(sl):
@@ -201,25 +201,29 @@ def test_needle_inside_prefix_and_decoy_outside():
     k[0, 0, n - 1] = unit * 60
     k[0, 0, n] = unit * 120       # decoy beyond the valid prefix
     case["k"] = k.to(torch.bfloat16)
-    got = run(case, out_dtype="f32", chunk_tokens=256).cpu()
+    got = run(case, out_dtype="f32", workgroups=13).cpu()
     for h in range(Hq):
         assert torch.allclose(got[0, h], case["v"][0, 0, n - 1].float(), atol=2e-2)
 
 
 # ------------------------------------------------------------------------------ invariances
 @pytest.mark.parametrize("qd,kd", DTYPES)
-def test_chunk_length_invariance(qd, kd):
-    say(f"chunk invariance q={qd} kv={kd}")
-    case = workloads.make_case(2, 16, 4, 128, 2048, qd, kd, seq_lens=(2048, 1500), seed=21)
-    outs = [run(case, out_dtype="f32", chunk_tokens=c).cpu().double() for c in (256, 512, 1024, 2048)]
-    ref_scale = outs[-1].abs().max()
-    # The f32 path carries the softmax weights in f32, so the split and merge must agree to f32
-    # rounding.  The matrix-core paths round each weight to bf16 against the running max of its own
-    # chunk, so different chunkings differ by up to about one bf16 unit (2^-8) of the output scale.
+def test_workgroup_count_invariance(qd, kd):
+    """Every way of cutting the cache over workgroups gives the same answer: 1 workgroup (no split),
+    counts that cut segments at odd places, and more workgroups than tiles."""
+    say(f"workgroup-count invariance q={qd} kv={kd}")
+    case = workloads.make_case(3, 16, 4, 128, 2048, qd, kd, seq_lens=(2048, 1500, 33), seed=21)
+    counts = (1, 2, 5, 64, 333, 512, 4096)
+    outs = [run(case, out_dtype="f32", workgroups=c).cpu().double() for c in counts]
+    ref_scale = outs[0].abs().max()
+    # The f32 path carries the softmax weights in f32, so every split must agree to f32 rounding.
+    # The matrix-core paths round each weight to bf16 against the running max of its own piece, so
+    # different splits differ by up to about one bf16 unit (2^-8) of the output scale.
     tol = 2e-5 if kd == "f32" else 2 ** -8
-    for o in outs[:-1]:
-        assert (o - outs[-1]).abs().max() <= tol * ref_scale
-    compare(outs[0], oracle_full(case), kd, "chunk 256")
+    for c, o in zip(counts[1:], outs[1:]):
+        assert (o - outs[0]).abs().max() <= tol * ref_scale, c
+    for c, o in zip(counts, outs):
+        compare(o, oracle_full(case), kd, f"{c} workgroups")
 
 
 def test_bitwise_determinism_and_batch_independence():
@@ -239,11 +243,11 @@ def test_token_permutation_invariance():
     say("permutation")
     n = 1000
     case = workloads.make_case(1, 16, 2, 128, 1024, "bf16", "bf16", seq_lens=(n,), seed=2)
-    a = run(case, out_dtype="f32", chunk_tokens=256).cpu().double()
+    a = run(case, out_dtype="f32", workgroups=13).cpu().double()
     perm = torch.randperm(n, generator=torch.Generator().manual_seed(0))
     case["k"][0, :, :n] = case["k"][0, :, perm]
     case["v"][0, :, :n] = case["v"][0, :, perm]
-    b = run(case, out_dtype="f32", chunk_tokens=256).cpu().double()
+    b = run(case, out_dtype="f32", workgroups=13).cpu().double()
     assert (a - b).abs().max() <= 5e-3 * a.abs().max()
 
 
@@ -263,26 +267,42 @@ def test_output_guards_and_workspace_counters():
     n = 2 * 16 * 128
     buf = torch.full((n + 2 * 4096,), -7.0, dtype=torch.float32, device=DEV)
     out = buf[4096:4096 + n].view(2, 16, 128)
-    shape = gqa.make_shape(2, 16, 4, 1200, 128, gqa.BF16, gqa.BF16, gqa.F32, chunk_tokens=256)
+    shape = gqa.make_shape(2, 16, 4, 1200, 128, gqa.BF16, gqa.BF16, gqa.F32, num_workgroups=13)
     ws = torch.zeros(gqa.workspace_bytes(shape) + 8192, dtype=torch.uint8, device=DEV)
     ws[-8192:] = 0xA5
-    gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"], case["scale"], out=out, chunk_tokens=256,
+    gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"], case["scale"], out=out, num_workgroups=13,
                workspace=ws)
     torch.cuda.synchronize()
     assert (buf[:4096] == -7.0).all() and (buf[4096 + n:] == -7.0).all()
     assert (ws[-8192:] == 0xA5).all()
-    assert (ws[: 2 * 4 * 4] == 0).all()      # per-(b, KV head) counters back at zero
+    assert (ws[: 1 << 20] == 0).all()        # the counter area is back at zero
     compare(out, oracle_full(case), "bf16", "guarded")
 
 
 def test_workspace_init_clears_counters():
     say("workspace init")
-    shape = gqa.make_shape(2, 16, 4, 1200, 128, gqa.BF16, gqa.BF16, chunk_tokens=256)
+    shape = gqa.make_shape(2, 16, 4, 1200, 128, gqa.BF16, gqa.BF16, num_workgroups=13)
     ws = torch.full((gqa.workspace_bytes(shape),), 0x11, dtype=torch.uint8, device=DEV)
     import ctypes
     assert gqa.lib.gqa_workspace_init(ws.data_ptr(), ws.numel(), ctypes.byref(shape), None) == 0
     torch.cuda.synchronize()
-    assert (ws[:32] == 0).all() and (ws[256:512] == 0x11).all()
+    assert (ws[:32] == 0).all() and (ws[1 << 20:(1 << 20) + 256] == 0x11).all()
+
+
+def test_one_workspace_serves_shapes_in_any_order():
+    """A workspace last used by another shape (whose partial results fill its slots) must still give
+    exact results: counters never share bytes with any shape's partial results."""
+    say("workspace reuse across shapes")
+    big = workloads.make_case(2, 8, 2, 128, 4000, "bf16", "bf16", seq_lens=(4000, 3900), seed=40)
+    many = workloads.make_case(24, 32, 8, 128, 600, "bf16", "bf16", seq_lens=tuple(range(577, 601)),
+                               seed=41)
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device=DEV)
+    for case, wg in ((big, 64), (many, 128), (big, 512), (many, 37)):
+        d = to_dev(case)
+        out = gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"], case["scale"], out_dtype=torch.float32,
+                         num_workgroups=wg, workspace=ws)
+        torch.cuda.synchronize()
+        compare(out, oracle_full(case), "bf16", f"B{case['B']} after reuse, {wg} workgroups")
 
 
 def test_out_of_range_seq_lens_are_clamped_and_reported():
@@ -329,7 +349,7 @@ def _sample_rows(case, extra=16, seed=0):
 @pytest.mark.parametrize("wid", [1, 2, 3, "4-mha", "4-gqa", "4-mqa", 5])
 def test_workload_parity(wid):
     """Each named workload at full size, in the launch configuration the benchmark times (library's
-    chunk choice); the oracle checks every row of workload 1 and a sample of rows otherwise."""
+    workgroup count); the oracle checks every row of workload 1 and a sample of rows otherwise."""
     w = workloads.WORKLOADS[wid]
     say(f"workload {wid}: {w.name}")
     case = workloads.make(wid)
@@ -343,4 +363,8 @@ def test_workload_parity(wid):
                            rows, case["q_dtype"], case["kv_dtype"], case["k_descale"],
                            case["v_descale"])
     sel = torch.stack([got[b, h] for b, h in rows])
+    bad = [rows[i] for i in range(len(rows))
+           if not np.abs(sel[i].double().numpy() - want[i]).max() <= ABS_GATE[w.kv_dtype]]
+    if bad:
+        say(f"  rows off the oracle: {bad}; seq_lens {case['seq_lens'].tolist()}")
     compare(sel, want, w.kv_dtype, f"workload {wid} {len(rows)} rows")
