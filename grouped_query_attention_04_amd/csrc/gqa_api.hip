@@ -39,7 +39,7 @@ struct Layout {
 Layout plan(const gqa_shape_t* s) {
   Layout lo;
   lo.workgroups = plan_workgroups(s);
-  const size_t slots = (size_t)lo.workgroups * 2;
+  const size_t slots = (size_t)lo.workgroups * 2;  // two per workgroup
   const size_t G = (size_t)(s->Hq / s->Hkv);
   lo.counters_off = 0;
   lo.ml_off = kMaxUnits * sizeof(uint32_t);

@@ -16,7 +16,9 @@
 // is a whole segment is normalised and stored at once.  A piece of a segment that several
 // workgroups share is published to the workspace; the workgroup that finishes a segment's last
 // piece -- found with one atomic counter per (b, j) -- merges the pieces in workgroup order and
-// stores the output.  Nothing waits on another workgroup.
+// stores the output.  Nothing waits on another workgroup.  Two workgroups fit on a compute unit
+// (at most 256 registers per lane), so one's pauses at piece ends can overlap with the other's
+// streaming when more than one workgroup per compute unit is launched.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -100,6 +102,10 @@ __device__ __forceinline__ float wave_sum_xor_16_32(float x) {
   return x + __shfl_xor(x, 32);
 }
 
+// Values every lane agrees on are moved to scalar registers, so that everything derived from them
+// (buffer descriptors in particular) stays uniform in the compiler's view.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 template <typename OutT>
 __device__ __forceinline__ void store_out(OutT* p, float x);
 template <>
@@ -107,6 +113,18 @@ __device__ __forceinline__ void store_out<float>(float* p, float x) { *p = x; }
 template <>
 __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float x) {
   *p = (uint16_t)float_to_bf16_bits(x);
+}
+// Four consecutive outputs (16-byte aligned for f32, 8-byte aligned for bf16).
+template <typename OutT>
+__device__ __forceinline__ void store_out4(OutT* p, f32x4_t x);
+template <>
+__device__ __forceinline__ void store_out4<float>(float* p, f32x4_t x) {
+  *reinterpret_cast<f32x4_t*>(p) = x;
+}
+template <>
+__device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, f32x4_t x) {
+  *reinterpret_cast<u32x2_t*>(p) = u32x2_t{float_to_bf16_bits(x[0]) | (float_to_bf16_bits(x[1]) << 16),
+                                           float_to_bf16_bits(x[2]) | (float_to_bf16_bits(x[3]) << 16)};
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -136,7 +154,7 @@ __device__ int block_sum(int x, Shared& sh) {
 #pragma unroll
   for (int i = 0; i < NTH / 64; ++i) t += sh.red[i];
   __syncthreads();
-  return t;
+  return uniform(t);
 }
 
 // Inclusive prefix sum over the workgroup's threads (thread order); *total receives the sum.
@@ -156,7 +174,7 @@ __device__ int block_scan(int x, Shared& sh, int* total) {
     t += sh.red[i];
   }
   __syncthreads();
-  *total = t;
+  *total = uniform(t);
   return x + before;
 }
 
@@ -171,7 +189,7 @@ struct Range {
 __device__ __forceinline__ long long range_lo(long long w, long long T, int weff) { return w * T / weff; }
 // Workgroup whose range holds tile x: the largest w with range_lo(w) <= x.
 __device__ __forceinline__ int range_owner(long long x, long long T, int weff) {
-  return (int)(((x + 1) * weff - 1) / T);
+  return uniform((int)(((x + 1) * weff - 1) / T));
 }
 
 template <int TILE, int NTH>
@@ -200,8 +218,8 @@ __device__ bool find_range(const Params& p, Shared& sh, Range& r) {
     __syncthreads();
     if ((long long)p.Hkv * carry > r.lo) break;
   }
-  r.b = sh.found_b;
-  r.pre = sh.found_pre;
+  r.b = uniform(sh.found_b);
+  r.pre = uniform(sh.found_pre);
   return true;
 }
 
@@ -209,7 +227,7 @@ __device__ bool find_range(const Params& p, Shared& sh, Range& r) {
 template <int D, typename OutT, int NTH>
 __device__ void zero_empty_rows(const Params& p) {
   for (int b = blockIdx.x; b < p.B; b += p.W) {
-    if (seq_len(p, b) != 0) continue;
+    if (uniform(seq_len(p, b)) != 0) continue;
     OutT* out = reinterpret_cast<OutT*>(p.out) + (size_t)b * p.Hq * D;
     for (int i = threadIdx.x; i < p.Hq * D; i += NTH) store_out(out + i, 0.f);
   }
@@ -239,12 +257,13 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
   constexpr int kRow = EpiLayout<GT, D, NW>::kRow;
   const int tid = threadIdx.x;
   const int G = p.G;
+  const int nitems = G * D / 4;  // groups of 4 consecutive columns of one query row
   const float* ep_m = ep;
   const float* ep_l = ep + NW * GT;
   const float* ep_o = ep + 2 * NW * GT;
   OutT* out = reinterpret_cast<OutT*>(p.out) + ((size_t)pc.b * p.Hq + (size_t)pc.j * G) * D;
 
-  // merge of the NW wave states for 4 consecutive columns of one query row
+  // merge of the NW wave states for one item
   auto merge4 = [&](int item, float& M, float& l, f32x4_t& o) {
     const int g = (4 * item) / D, cc = (4 * item) % D;
     M = -INFINITY;
@@ -263,23 +282,20 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
   const int wfirst = range_owner(pc.s, r.T, r.weff);
   const int wlast = range_owner(pc.e - 1, r.T, r.weff);
   if (wfirst == wlast) {  // the whole segment was here: normalise and store
-    for (int item = tid; item < G * D / 4; item += NTH) {
+    for (int item = tid; item < nitems; item += NTH) {
       float M, l;
       f32x4_t o;
       merge4(item, M, l, o);
-      const float inv = p.v_descale / l;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) store_out(out + 4 * item + e, o[e] * inv);
+      store_out4(out + 4 * item, o * (p.v_descale / l));
     }
     return;
   }
 
   // A shared segment: publish this piece with agent-scope stores.
   const size_t slot = (size_t)blockIdx.x * 2 + pc.slot;
-  float* po = p.part_o + slot * G * D;
   float* pml = p.part_ml + slot * G * 2;
-  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(po, G * D * 4);
-  for (int item = tid; item < G * D / 4; item += NTH) {
+  const __amdgpu_buffer_rsrc_t rpo = make_rsrc(p.part_o + slot * G * D, G * D * 4);
+  for (int item = tid; item < nitems; item += NTH) {
     float M, l;
     f32x4_t o;
     merge4(item, M, l, o);
@@ -302,45 +318,62 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
     sh.last = (done == (uint32_t)(wlast - wfirst));
   }
   __syncthreads();
-  if (!sh.last) return;
+  if (!uniform(sh.last)) return;
   // Acquire at agent scope: drop this XCD's cached copies of the workspace lines, so the loads
   // below see what the other workgroups wrote through to memory.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  // Last piece of the segment: log-sum-exp merge of its pieces in workgroup order.
+  // Last piece of the segment: log-sum-exp merge of its pieces in workgroup order.  The piece loop
+  // is the outer (uniform) loop so that each piece's buffer descriptor stays scalar; every thread
+  // carries the running (max, sum, output) of its NI items, with the loads of PB pieces in flight.
+  constexpr int NI = (GT * D / 4 + NTH - 1) / NTH;
+  constexpr int PB = 4;
   const int npc = wlast - wfirst + 1;
-  for (int item = tid; item < G * D / 4; item += NTH) {
-    const int g = (4 * item) / D;
-    float acc_m = -INFINITY, acc_l = 0.f;
-    f32x4_t acc_o = {0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < npc; k0 += 4) {  // four pieces' loads in flight per thread
-      float m[4], l[4];
-      u32x4_t o[4];
+  float acc_m[NI], acc_l[NI];
+  f32x4_t acc_o[NI];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int w = wfirst + (k0 + u < npc ? k0 + u : 0);
-        // the segment's piece in workgroup w is its slot 1 only when the segment starts inside
-        // w's range, i.e. after w's first tile
-        const size_t sl = (size_t)w * 2 + (pc.s > range_lo(w, r.T, r.weff) ? 1 : 0);
-        m[u] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        l[u] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        o[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                   make_rsrc(p.part_o + sl * G * D, G * D * 4), item * 16, 0, kAgentScope));
-      }
+  for (int i = 0; i < NI; ++i) {
+    acc_m[i] = -INFINITY;
+    acc_l[i] = 0.f;
+    acc_o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int k0 = 0; k0 < npc; k0 += PB) {
+    float m[PB][NI], l[PB][NI];
+    u32x4_t o[PB][NI];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (k0 + u >= npc) break;
-        const float mn = fmaxf(acc_m, m[u]);
-        const float a = __builtin_amdgcn_exp2f(acc_m - mn);
-        const float s = __builtin_amdgcn_exp2f(m[u] - mn);
-        acc_l = acc_l * a + l[u] * s;
-        acc_o = acc_o * a + __builtin_bit_cast(f32x4_t, o[u]) * s;
-        acc_m = mn;
+    for (int u = 0; u < PB; ++u) {
+      const int w = wfirst + (k0 + u < npc ? k0 + u : 0);
+      // the segment's piece in workgroup w is its slot 1 only when the segment starts inside w's
+      // range, i.e. after w's first tile
+      const size_t sl = (size_t)uniform(w * 2 + (pc.s > range_lo(w, r.T, r.weff) ? 1 : 0));
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.part_o + sl * G * D, G * D * 4);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int item = tid + i * NTH;
+        const int g = (4 * (item < nitems ? item : 0)) / D;
+        m[u][i] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        l[u][i] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        o[u][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, item * 16, 0, kAgentScope));
       }
     }
-    const float inv = p.v_descale / acc_l;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_out(out + 4 * item + e, acc_o[e] * inv);
+    for (int u = 0; u < PB; ++u) {
+      if (k0 + u >= npc) break;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const float mn = fmaxf(acc_m[i], m[u][i]);
+        const float a = __builtin_amdgcn_exp2f(acc_m[i] - mn);
+        const float sc = __builtin_amdgcn_exp2f(m[u][i] - mn);
+        acc_l[i] = acc_l[i] * a + l[u][i] * sc;
+        acc_o[i] = acc_o[i] * a + __builtin_bit_cast(f32x4_t, o[u][i]) * sc;
+        acc_m[i] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int item = tid + i * NTH;
+    if (item < nitems) store_out4(out + 4 * item, acc_o[i] * (p.v_descale / acc_l[i]));
   }
   if (tid == 0) __hip_atomic_store(p.counters + bj, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -350,7 +383,7 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
 template <int TILE, int NTH, typename Body>
 __device__ void for_each_piece(const Params& p, const Range& r, Body&& body) {
   int b = r.b, pre = r.pre;
-  int tb = seq_tiles<TILE>(p, b);
+  int tb = uniform(seq_tiles<TILE>(p, b));
   const long long row0 = (long long)p.Hkv * pre;
   int j = (int)((r.lo - row0) / tb);
   long long seg = row0 + (long long)j * tb;
@@ -364,7 +397,7 @@ __device__ void for_each_piece(const Params& p, const Range& r, Body&& body) {
     pc.s = seg;
     pc.e = seg_end;
     pc.slot = cur == r.lo ? 0 : 1;
-    body(pc, (int)(cur - seg), (int)(pend - cur), seq_len(p, b));
+    body(pc, (int)(cur - seg), (int)(pend - cur), uniform(seq_len(p, b)));
     cur = pend;
     if (cur >= r.hi) break;
     if (++j == p.Hkv) {
@@ -372,7 +405,7 @@ __device__ void for_each_piece(const Params& p, const Range& r, Body&& body) {
       pre += tb;
       do {
         ++b;
-        tb = seq_tiles<TILE>(p, b);
+        tb = uniform(seq_tiles<TILE>(p, b));
       } while (tb == 0);
       seg = (long long)p.Hkv * pre;
     } else {
@@ -384,24 +417,25 @@ __device__ void for_each_piece(const Params& p, const Range& r, Body&& body) {
 // ------------------------------------------------------------------------------------------------
 // bf16 / fp8 cache: matrix-core kernel.
 //
-// Per 32-token tile and wave (lane l, quad q = l / 16, r = l % 16):
+// Per 16-token tile and wave (lane l, quad q = l / 16, r = l % 16):
 //   QK^T on v_mfma_f32_16x16x32_bf16 with A = K tile (M = tokens, K = head dim) loaded straight from
 //   HBM into the A-operand layout, and B = Q^T (N = query rows of the group, zero-padded to 16).
-//   The result leaves lane l holding S[g = r][t = 16h + 4q + i].
-//   PV on the same instruction with A = V^T (M = head-dim columns, K = tokens) read from a per-wave
-//   LDS copy of the tile with ds_read_b64_tr_b16, and B = P^T, which is exactly S's register layout
-//   after exp2 and a bf16 pack.  The accumulator O^T leaves lane l holding O[g = r][c = 16m + 4q + i],
-//   so the running max / sum of row g live in the same lanes as its outputs.
+//   The result leaves lane l holding S[g = r][t = 4q + i].
+//   PV on v_mfma_f32_16x16x16_bf16 with A = V^T (M = head-dim columns, K = tokens) read from a
+//   per-wave LDS copy of the tile with ds_read_b64_tr_b16, and B = P^T, which is exactly S's
+//   register layout after exp2 and a bf16 pack.  The accumulator O^T leaves lane l holding
+//   O[g = r][c = 16m + 4q + i], so the running max / sum of row g live in the same lanes as its
+//   outputs.
 // NT = 16-row tiles of query rows (G <= 16 * NT).
 template <int D, int NT, bool FP8, typename OutT, int NW>
-__global__ void __launch_bounds__(NW * 64, 1) decode_mfma_kernel(Params p) {
-  constexpr int TILE = 32;
+__global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(Params p) {
+  constexpr int TILE = 16;
   constexpr int NTH = NW * 64;
   constexpr int KS = D / 32;          // k-steps of QK^T
   constexpr int MT = D / 16;          // m-tiles of PV
   constexpr int ELT = FP8 ? 1 : 2;    // bytes per cache element
   constexpr int ROWB = D * ELT;       // bytes per cache row
-  constexpr int NK = 2 * D * ELT / 64;          // 16-byte K loads per lane per tile
+  constexpr int NK = D * ELT / 64;              // 16-byte K loads per lane per tile
   constexpr int NV = TILE * ROWB / (64 * 16);   // 16-byte V loads per lane per tile
   constexpr int CPR = D / 8;          // 16-byte bf16 chunks per row of the LDS V tile
   constexpr int VTILE = TILE * D * 2;            // bytes of one LDS V tile (bf16)
@@ -466,10 +500,8 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_kernel(Params p) {
       const bool live = it < mine;
       const uint32_t t0 = live ? (uint32_t)tile_start(it) : 0u;
 #pragma unroll
-      for (int x = 0; x < NK; ++x) {
-        // x = h * (NK/2) + u: token subtile h (16 rows), 16-byte column block u of this lane's quad
-        const int h = x / (NK / 2), u = x % (NK / 2);
-        const uint32_t off = (t0 + 16 * h + r) * ROWB + u * 64 + q * 16;
+      for (int x = 0; x < NK; ++x) {  // 16-byte column block x of this lane's quad, token row r
+        const uint32_t off = (t0 + r) * ROWB + x * 64 + q * 16;
         R.k[x] = load16(rk, live ? off : kNoTile);
       }
 #pragma unroll
@@ -498,82 +530,66 @@ __global__ void __launch_bounds__(NW * 64, 1) decode_mfma_kernel(Params p) {
         }
       }
       // -- K operands
-      bf16x8_t ak[2][KS];
+      bf16x8_t ak[KS];
 #pragma unroll
       for (int x = 0; x < NK; ++x) {
-        const int h = x / (NK / 2), u = x % (NK / 2);
         if constexpr (!FP8) {
-          ak[h][u] = __builtin_bit_cast(bf16x8_t, R.k[x]);
+          ak[x] = __builtin_bit_cast(bf16x8_t, R.k[x]);
         } else {
           const u32x4_t a = R.k[x];
-          ak[h][2 * u] = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(a[0], a[1]));
-          ak[h][2 * u + 1] = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(a[2], a[3]));
+          ak[2 * x] = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(a[0], a[1]));
+          ak[2 * x + 1] = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(a[2], a[3]));
         }
       }
       // -- scores S^T = K Q^T
-      f32x4_t sc[2][NT];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[h][s], bq[nt][s], acc, 0, 0, 0);
-          sc[h][nt] = acc * p.qk_scale;
-        }
-      if (t0 + TILE > n) {  // ragged last tile: positions >= n get no weight
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (t0 + 16 * h + 4 * q + i >= n)
-#pragma unroll
-              for (int nt = 0; nt < NT; ++nt) sc[h][nt][i] = -INFINITY;
-      }
-      // -- online softmax; P^T packed to bf16 in the B-operand layout of PV
-      bf16x8_t bp[NT];
+      f32x4_t sc[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][nt][0], sc[0][nt][1]), fmaxf(sc[0][nt][2], sc[0][nt][3])),
-                         fmaxf(fmaxf(sc[1][nt][0], sc[1][nt][1]), fmaxf(sc[1][nt][2], sc[1][nt][3])));
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[s], bq[nt][s], acc, 0, 0, 0);
+        sc[nt] = acc * p.qk_scale;
+      }
+      if (t0 + TILE > n) {  // ragged last tile: positions >= n get no weight
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + 4 * q + i >= n)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) sc[nt][i] = -INFINITY;
+      }
+      // -- online softmax; P^T packed to bf16 in the B-operand layout of PV
+      i16x4_t bp[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float mx = fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3]));
         mx = wave_max_xor_16_32(mx);
         const float m_new = fmaxf(m_run[nt], mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
         m_run[nt] = m_new;
-        uint32_t pk[4];
+        uint32_t pk[2];
         float psum = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i2 = 0; i2 < 2; ++i2) {
-            const uint32_t lo = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[h][nt][2 * i2] - m_new));
-            const uint32_t hi = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[h][nt][2 * i2 + 1] - m_new));
-            psum += bf16_bits_to_float(lo) + bf16_bits_to_float(hi);  // sum the weights actually used
-            pk[2 * h + i2] = lo | (hi << 16);
-          }
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const uint32_t lo = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[nt][2 * i2] - m_new));
+          const uint32_t hi = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[nt][2 * i2 + 1] - m_new));
+          psum += bf16_bits_to_float(lo) + bf16_bits_to_float(hi);  // sum the weights actually used
+          pk[i2] = lo | (hi << 16);
+        }
         l_run[nt] = l_run[nt] * alpha + psum;
-        bp[nt] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+        bp[nt] = __builtin_bit_cast(i16x4_t, u32x2_t{pk[0], pk[1]});
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
       }
-      // -- O^T += V^T P^T, V^T read transposed from LDS
+      // -- O^T += V^T P^T, V^T read transposed from LDS (rows 4q..4q+3 = tokens, column 16m + r)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        uint32_t a[4];
+        const int row = 4 * q + r / 4;
+        const int col = 16 * mt + 4 * (r % 4);
+        const int pos = (col / 8) ^ (2 * (row % (D / 16)));
+        const uint32_t addr = vt_lds + row * D * 2 + pos * 16 + (col % 8) * 2;
+        const i16x4_t av = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS i16x4_t*)(uintptr_t)addr);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 16 * h + 4 * q + r / 4;
-          const int col = 16 * mt + 4 * (r % 4);
-          const int pos = (col / 8) ^ (2 * (row % (D / 16)));
-          const uint32_t addr = vt_lds + row * D * 2 + pos * 16 + (col % 8) * 2;
-          const i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS i16x4_t*)(uintptr_t)addr);
-          const u32x2_t tt = __builtin_bit_cast(u32x2_t, t);
-          a[2 * h] = tt[0];
-          a[2 * h + 1] = tt[1];
-        }
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{a[0], a[1], a[2], a[3]});
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[nt], o[nt][mt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bp[nt], o[nt][mt], 0, 0, 0);
       }
     };
 

@@ -80,7 +80,7 @@ def test_workspace_grows_with_workgroups_and_is_aligned():
     b = gqa.workspace_bytes(_shape(L=4096, num_workgroups=256))
     assert a > 0 and b > a and a % 256 == 0 and b % 256 == 0
     # fixed counter area + two slots per workgroup of (m, l) and d floats per query row
-    slots, G, d = 512, 4, 64
+    slots, G, d = 2 * 256, 4, 64
     assert b >= (1 << 20) + slots * G * (2 + d) * 4
     assert b - a == 2 * (256 - 64) * G * (2 + d) * 4
     assert gqa.workspace_bytes(_shape(L=4096)) == gqa.workspace_bytes(_shape(L=4096, num_workgroups=256))

@@ -296,7 +296,7 @@ def test_one_workspace_serves_shapes_in_any_order():
     big = workloads.make_case(2, 8, 2, 128, 4000, "bf16", "bf16", seq_lens=(4000, 3900), seed=40)
     many = workloads.make_case(24, 32, 8, 128, 600, "bf16", "bf16", seq_lens=tuple(range(577, 601)),
                                seed=41)
-    ws = torch.zeros(8 << 20, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(32 << 20, dtype=torch.uint8, device=DEV)
     for case, wg in ((big, 64), (many, 128), (big, 512), (many, 37)):
         d = to_dev(case)
         out = gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"], case["scale"], out_dtype=torch.float32,
