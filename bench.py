@@ -39,10 +39,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on the
-    kernel sources as they are now; otherwise None."""
-    if not os.path.exists(TRAFFIC_SUMMARY):
+def recorded_traffic(wid, workgroups):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on this
+    workload and launch configuration with the kernel sources as they are now; otherwise None."""
+    if wid != 3 or workgroups != 0 or not os.path.exists(TRAFFIC_SUMMARY):
         return None
     text = open(TRAFFIC_SUMMARY).read()
     src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
@@ -184,7 +184,7 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {args.calib_copy_mib} MiB done")
 
-    traffic = recorded_traffic()
+    traffic = recorded_traffic(wid, args.workgroups)
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
