@@ -6,6 +6,9 @@ seq_lens ~ U[6000, 8192], bf16) with inputs resident in HBM.  The KV bytes of a 
 sum_b seq_lens[b] * Hkv * 2 * d * 2 (one K and one V row per cached token and KV head).  Several
 copies of the cache are rotated so that no step finds its cache in the 256 MB last-level cache.
 
+With --paged BS the same workload is laid out in pages of BS positions placed by a seeded random
+permutation (gqa_decode_paged); the KV bytes counted are the same.
+
 Prints one JSON line on stdout (diagnostics go to stderr).
 """
 import argparse
@@ -52,15 +55,20 @@ def recorded_traffic(wid, workgroups):
     return float(val.group(1))
 
 
-def cpu_baseline(case, groups_b):
+def cpu_baseline(case, groups_b, paged=None):
     """Time the fp64 oracle (single thread) on every query head of batch entries [0, groups_b)."""
     from oracle import ref
 
     rows = [(b, h) for b in range(groups_b) for h in range(case["Hq"])]
     sl = case["seq_lens"].numpy()
     t0 = time.perf_counter()
-    ref.decode_rows(case["q"], case["k"], case["v"], sl, case["scale"], rows, case["q_dtype"],
-                    case["kv_dtype"], case["k_descale"], case["v_descale"])
+    if paged is None:
+        ref.decode_rows(case["q"], case["k"], case["v"], sl, case["scale"], rows, case["q_dtype"],
+                        case["kv_dtype"], case["k_descale"], case["v_descale"])
+    else:
+        ref.decode_paged(case["q"], paged["k_pages"], paged["v_pages"], paged["block_table"].numpy(), sl,
+                         case["scale"], rows, case["q_dtype"], case["kv_dtype"], case["k_descale"],
+                         case["v_descale"])
     dt = time.perf_counter() - t0
     elt = 1 if case["kv_dtype"] == "fp8_e4m3" else (4 if case["kv_dtype"] == "f32" else 2)
     kv_bytes = int(sl[:groups_b].sum()) * case["Hkv"] * 2 * case["d"] * elt
@@ -78,6 +86,8 @@ def main():
     ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4-mha, 4-gqa, 4-mqa, 5)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated (0 = enough for 2 GiB)")
     ap.add_argument("--workgroups", type=int, default=0, help="workgroups (0 = library choice)")
+    ap.add_argument("--paged", type=int, default=0, metavar="BS",
+                    help="lay the cache out in pages of BS positions (0 = dense cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=16)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -104,18 +114,30 @@ def main():
     elt = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
     sl = case["seq_lens"]
     kv_bytes = int(sl.sum()) * w.Hkv * 2 * w.d * elt
-    alloc = 2 * case["k"].numel() * elt
+    paged = None
+    if args.paged:
+        paged = workloads.paginate(case, args.paged, seed=w.seed + 100)
+        kc, vc = paged["k_pages"], paged["v_pages"]
+    else:
+        kc, vc = case["k"], case["v"]
+    alloc = 2 * kc.numel() * elt
     copies = args.copies or max(2, -(-(2 << 30) // alloc))
 
     q = case["q"].to(dev)
     seq = sl.to(dev)
-    ks = [case["k"].to(dev) for _ in range(copies)]
-    vs = [case["v"].to(dev) for _ in range(copies)]
+    ks = [kc.to(dev) for _ in range(copies)]
+    vs = [vc.to(dev) for _ in range(copies)]
     od = workloads.TORCH_DTYPES[w.out_dtype]
     out = torch.empty(w.B, w.Hq, w.d, dtype=od, device=dev)
     code = {"f32": gqa.F32, "bf16": gqa.BF16, "fp8_e4m3": gqa.FP8_E4M3}
-    shape = gqa.make_shape(w.B, w.Hq, w.Hkv, w.L, w.d, code[w.q_dtype], code[w.kv_dtype],
-                           code[w.out_dtype], num_workgroups=args.workgroups)
+    if paged:
+        table = paged["block_table"].to(dev)
+        shape = gqa.make_paged_shape(w.B, w.Hq, w.Hkv, w.d, args.paged, table.shape[1], paged["num_blocks"],
+                                     code[w.q_dtype], code[w.kv_dtype], code[w.out_dtype],
+                                     num_workgroups=args.workgroups)
+    else:
+        shape = gqa.make_shape(w.B, w.Hq, w.Hkv, w.L, w.d, code[w.q_dtype], code[w.kv_dtype],
+                               code[w.out_dtype], num_workgroups=args.workgroups)
     ws = torch.zeros(gqa.workspace_bytes(shape), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
@@ -125,8 +147,13 @@ def main():
     scale = float(case["scale"])
 
     def step(i):
-        rc = gqa.lib.gqa_decode(q.data_ptr(), kptr[i % copies], vptr[i % copies], seq.data_ptr(), scale,
-                                out.data_ptr(), shape_ref, ws.data_ptr(), ws.numel(), sh)
+        if paged:
+            rc = gqa.lib.gqa_decode_paged(q.data_ptr(), kptr[i % copies], vptr[i % copies], table.data_ptr(),
+                                          seq.data_ptr(), scale, out.data_ptr(), shape_ref, ws.data_ptr(),
+                                          ws.numel(), sh)
+        else:
+            rc = gqa.lib.gqa_decode(q.data_ptr(), kptr[i % copies], vptr[i % copies], seq.data_ptr(), scale,
+                                    out.data_ptr(), shape_ref, ws.data_ptr(), ws.numel(), sh)
         if rc:
             raise RuntimeError(gqa.status_string(rc))
 
@@ -184,13 +211,15 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {args.calib_copy_mib} MiB done")
 
-    traffic = recorded_traffic(wid, args.workgroups)
+    traffic = None if paged else recorded_traffic(wid, args.workgroups)
+    layout = f"paged, {args.paged} positions per page, random page placement" if paged else "dense"
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.kv_dtype, "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L,
+        "config": {"workload": w.name + (f" paged bs{args.paged}" if paged else ""), "cache_layout": layout,
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L,
                    "seq_lens": f"sum {int(sl.sum())} (min {int(sl.min())}, max {int(sl.max())})",
                    "kv_bytes_per_step": kv_bytes, "cache_copies": copies,
                    "parallelism": "single GPU"},
@@ -200,7 +229,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the same workload")
-        result["cpu_baseline"] = cpu_baseline(case, min(args.cpu_sample_batches, w.B))
+        result["cpu_baseline"] = cpu_baseline(case, min(args.cpu_sample_batches, w.B), paged)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -8,7 +8,8 @@ supplies device memory and the current stream.  The library must have been built
 ``out[b, h] = softmax(scale * q[b, h] . k_cache[b, h // G, :n]) @ v_cache[b, h // G, :n]`` with
 ``n = seq_lens[b]`` -- scaled dot-product attention per query head, contiguous groups of G query heads
 sharing one KV head ("Grouped-Query Attention: How Sharing KV Heads Shrinks Inference Memory",
-section "How grouped-query attention works").
+section "How grouped-query attention works").  ``decode_paged`` computes the same over a cache kept in
+fixed-size pages addressed through a block table.
 """
 import ctypes
 import math
@@ -39,8 +40,18 @@ class Shape(ctypes.Structure):
                 ("num_workgroups", ctypes.c_int32)]
 
 
+class PagedShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+                ("kv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("k_descale", ctypes.c_float), ("v_descale", ctypes.c_float),
+                ("num_workgroups", ctypes.c_int32)]
+
+
 EXPORTS = ["gqa_shape_check", "gqa_decode_workspace_bytes", "gqa_workspace_init", "gqa_decode",
-           "gqa_kv_bytes_per_token", "gqa_validate_seq_lens", "gqa_stream_read",
+           "gqa_paged_shape_check", "gqa_decode_paged_workspace_bytes", "gqa_paged_workspace_init",
+           "gqa_decode_paged", "gqa_kv_bytes_per_token", "gqa_validate_seq_lens", "gqa_stream_read",
            "gqa_stream_read_sink_words", "gqa_status_string"]
 
 
@@ -58,6 +69,15 @@ def _load():
     lib.gqa_workspace_init.restype = ctypes.c_int
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, pS, vp, sz, vp]
     lib.gqa_decode.restype = ctypes.c_int
+    pP = ctypes.POINTER(PagedShape)
+    lib.gqa_paged_shape_check.argtypes = [pP]
+    lib.gqa_paged_shape_check.restype = ctypes.c_int
+    lib.gqa_decode_paged_workspace_bytes.argtypes = [pP]
+    lib.gqa_decode_paged_workspace_bytes.restype = sz
+    lib.gqa_paged_workspace_init.argtypes = [vp, sz, pP, vp]
+    lib.gqa_paged_workspace_init.restype = ctypes.c_int
+    lib.gqa_decode_paged.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, pP, vp, sz, vp]
+    lib.gqa_decode_paged.restype = ctypes.c_int
     lib.gqa_kv_bytes_per_token.argtypes = [ctypes.c_uint32] * 4
     lib.gqa_kv_bytes_per_token.restype = ctypes.c_uint64
     lib.gqa_validate_seq_lens.argtypes = [vp, i32, i32, vp, vp]
@@ -89,11 +109,21 @@ def make_shape(B, Hq, Hkv, L, d, q_dtype=BF16, kv_dtype=BF16, out_dtype=None, k_
                  k_descale, v_descale, num_workgroups)
 
 
-def shape_check(shape: Shape) -> int:
+def make_paged_shape(B, Hq, Hkv, d, block_size, max_blocks, num_blocks, q_dtype=BF16, kv_dtype=BF16,
+                     out_dtype=None, k_descale=1.0, v_descale=1.0, num_workgroups=0) -> PagedShape:
+    return PagedShape(B, Hq, Hkv, d, block_size, max_blocks, num_blocks, q_dtype, kv_dtype,
+                      q_dtype if out_dtype is None else out_dtype, k_descale, v_descale, num_workgroups)
+
+
+def shape_check(shape) -> int:
+    if isinstance(shape, PagedShape):
+        return lib.gqa_paged_shape_check(ctypes.byref(shape))
     return lib.gqa_shape_check(ctypes.byref(shape))
 
 
-def workspace_bytes(shape: Shape) -> int:
+def workspace_bytes(shape) -> int:
+    if isinstance(shape, PagedShape):
+        return lib.gqa_decode_paged_workspace_bytes(ctypes.byref(shape))
     return lib.gqa_decode_workspace_bytes(ctypes.byref(shape))
 
 
@@ -108,7 +138,7 @@ def _stream_handle(device):
 _workspaces = {}
 
 
-def workspace_for(shape: Shape, device) -> torch.Tensor:
+def workspace_for(shape, device) -> torch.Tensor:
     """A workspace cached per (device, stream), zeroed when allocated and grown when a shape needs
     more.  The library leaves its counters at zero after every call, so one buffer serves every
     shape.  Calls that overlap in time on different streams get different buffers."""
@@ -168,6 +198,52 @@ def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, *, out_dtype=Non
         _check(lib.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                               seq_lens.data_ptr(), float(scale), out.data_ptr(),
                               ctypes.byref(shape), ws.data_ptr(), ws.numel(), _stream_handle(dev)))
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=None, *, out_dtype=None,
+                 k_descale=1.0, v_descale=1.0, num_workgroups=0, workspace=None):
+    """Single-token GQA decode over a paged cache.  q [B,Hq,d]; k_pages, v_pages
+    [num_blocks,Hkv,block_size,d] (bf16 or fp8-e4m3); block_table [B,max_blocks] int32 (position t of
+    sequence b is row t % block_size of page block_table[b, t // block_size]); seq_lens [B] int32.
+    Returns out [B,Hq,d].  Enqueued on torch's current stream; no synchronisation."""
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError("expected q [B,Hq,d], k_pages and v_pages [num_blocks,Hkv,block_size,d]")
+    if k_pages.dtype != v_pages.dtype:
+        raise ValueError("k_pages and v_pages must share a dtype")
+    B, Hq, d = q.shape
+    num_blocks, Hkv, block_size, dk = k_pages.shape
+    if dk != d:
+        raise ValueError("head dim of q and the pages differ")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be an int32 tensor of shape [B, max_blocks]")
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
+        raise ValueError("seq_lens must be an int32 tensor of shape [B]")
+    tensors = [q, k_pages, v_pages, block_table, seq_lens] + ([out] if out is not None else [])
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must live on one CUDA (HIP) device")
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else q.dtype
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=out_dtype, device=dev)
+    elif out.shape != (B, Hq, d) or out.dtype != out_dtype:
+        raise ValueError("out must be [B,Hq,d] of dtype out_dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if q.dtype not in _CODE or k_pages.dtype not in _CODE or out_dtype not in _CODE:
+        raise TypeError(f"unsupported dtypes q={q.dtype} kv={k_pages.dtype} out={out_dtype}")
+    shape = make_paged_shape(B, Hq, Hkv, d, block_size, block_table.shape[1], num_blocks,
+                             _CODE[q.dtype], _CODE[k_pages.dtype], _CODE[out_dtype], k_descale,
+                             v_descale, num_workgroups)
+    ws = workspace if workspace is not None else workspace_for(shape, dev)
+    with torch.cuda.device(dev):
+        _check(lib.gqa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                    block_table.data_ptr(), seq_lens.data_ptr(), float(scale),
+                                    out.data_ptr(), ctypes.byref(shape), ws.data_ptr(), ws.numel(),
+                                    _stream_handle(dev)))
     return out
 
 

@@ -56,16 +56,78 @@ gqa_status_t launch(K kernel, int grid, const gqa::Params& prm, hipStream_t stre
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
-template <int D, int NT, bool FP8>
+template <int D, int NT, bool FP8, bool PAGED>
 gqa_status_t dispatch_mfma_out(int out_dtype, int grid, const gqa::Params& prm, hipStream_t st) {
-  if (out_dtype == GQA_BF16) return launch(gqa::decode_mfma_kernel<D, NT, FP8, uint16_t, kWaves>, grid, prm, st);
-  return launch(gqa::decode_mfma_kernel<D, NT, FP8, float, kWaves>, grid, prm, st);
+  if (out_dtype == GQA_BF16)
+    return launch(gqa::decode_mfma_kernel<D, NT, FP8, uint16_t, kWaves, PAGED>, grid, prm, st);
+  return launch(gqa::decode_mfma_kernel<D, NT, FP8, float, kWaves, PAGED>, grid, prm, st);
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool PAGED>
 gqa_status_t dispatch_mfma(int G, int out_dtype, int grid, const gqa::Params& prm, hipStream_t st) {
-  if (G <= 16) return dispatch_mfma_out<D, 1, FP8>(out_dtype, grid, prm, st);
-  return dispatch_mfma_out<D, 2, FP8>(out_dtype, grid, prm, st);
+  if (G <= 16) return dispatch_mfma_out<D, 1, FP8, PAGED>(out_dtype, grid, prm, st);
+  return dispatch_mfma_out<D, 2, FP8, PAGED>(out_dtype, grid, prm, st);
+}
+
+template <bool PAGED>
+gqa_status_t dispatch_mfma_dtype(int kv_dtype, int d, int G, int out_dtype, int grid, const gqa::Params& prm,
+                                 hipStream_t st) {
+  if (kv_dtype == GQA_BF16)
+    return d == 64 ? dispatch_mfma<64, false, PAGED>(G, out_dtype, grid, prm, st)
+                   : dispatch_mfma<128, false, PAGED>(G, out_dtype, grid, prm, st);
+  return d == 64 ? dispatch_mfma<64, true, PAGED>(G, out_dtype, grid, prm, st)
+                 : dispatch_mfma<128, true, PAGED>(G, out_dtype, grid, prm, st);
+}
+
+// The dense shape that a paged shape's kernels and workspace are planned with: L is the longest
+// sequence a page-table row can describe.
+gqa_shape_t dense_equivalent(const gqa_paged_shape_t* s) {
+  gqa_shape_t e;
+  e.B = s->B;
+  e.Hq = s->Hq;
+  e.Hkv = s->Hkv;
+  e.L = (int32_t)((long long)s->max_blocks * s->block_size);
+  e.d = s->d;
+  e.q_dtype = s->q_dtype;
+  e.kv_dtype = s->kv_dtype;
+  e.out_dtype = s->out_dtype;
+  e.k_descale = s->k_descale;
+  e.v_descale = s->v_descale;
+  e.num_workgroups = s->num_workgroups;
+  return e;
+}
+
+gqa::Params base_params(const void* q, const void* k, const void* v, const int32_t* seq_lens, float scale,
+                        void* out, const gqa_shape_t* s, const Layout& lo, void* workspace) {
+  gqa::Params prm;
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.seq_lens = seq_lens;
+  prm.out = out;
+  char* ws = static_cast<char*>(workspace);
+  prm.counters = reinterpret_cast<uint32_t*>(ws + lo.counters_off);
+  prm.part_ml = reinterpret_cast<float*>(ws + lo.ml_off);
+  prm.part_o = reinterpret_cast<float*>(ws + lo.o_off);
+  prm.B = s->B;
+  prm.Hq = s->Hq;
+  prm.Hkv = s->Hkv;
+  prm.L = s->L;
+  prm.G = s->Hq / s->Hkv;
+  prm.W = lo.workgroups;
+  prm.qk_scale = (float)((double)scale * (double)s->k_descale * 1.4426950408889634);
+  prm.v_descale = s->v_descale;
+  prm.block_table = nullptr;
+  prm.block_shift = 0;
+  prm.max_blocks = 0;
+  prm.num_blocks = 0;
+  return prm;
+}
+
+int log2_exact(int x) {
+  int k = 0;
+  while ((1 << k) < x) ++k;
+  return (1 << k) == x ? k : -1;
 }
 
 template <int D, int GT>
@@ -104,8 +166,8 @@ gqa_status_t gqa_shape_check(const gqa_shape_t* s) {
   if (!f32_path && !mfma_path) return GQA_ERR_UNSUPPORTED;
   // per-(batch, KV head) cache slices are addressed with 32-bit byte offsets
   if ((long long)s->L * s->d * elt_bytes(s->kv_dtype) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
-  // the tile space (tiles of 32 positions per batch entry and KV head) is indexed with 32-bit ints
-  if ((long long)s->B * s->Hkv * ((s->L + 31) / 32) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
+  // the tile space (tiles of 16 positions per batch entry and KV head) is counted with 32-bit ints
+  if ((long long)s->B * s->Hkv * ((s->L + 15) / 16) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
   if ((long long)s->B * s->Hq >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
   if ((size_t)s->B * s->Hkv > kMaxUnits) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
@@ -143,37 +205,67 @@ gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (!workspace || workspace_bytes < lo.total) return GQA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return GQA_ERR_INVALID_ARG;
 
-  gqa::Params prm;
-  prm.q = q;
-  prm.k = k_cache;
-  prm.v = v_cache;
-  prm.seq_lens = seq_lens;
-  prm.out = out;
-  char* ws = static_cast<char*>(workspace);
-  prm.counters = reinterpret_cast<uint32_t*>(ws + lo.counters_off);
-  prm.part_ml = reinterpret_cast<float*>(ws + lo.ml_off);
-  prm.part_o = reinterpret_cast<float*>(ws + lo.o_off);
-  prm.B = s->B;
-  prm.Hq = s->Hq;
-  prm.Hkv = s->Hkv;
-  prm.L = s->L;
-  prm.G = s->Hq / s->Hkv;
-  prm.W = lo.workgroups;
-  prm.qk_scale = (float)((double)scale * (double)s->k_descale * 1.4426950408889634);
-  prm.v_descale = s->v_descale;
-
+  const gqa::Params prm = base_params(q, k_cache, v_cache, seq_lens, scale, out, s, lo, workspace);
   const int grid = lo.workgroups;
   hipStream_t hs = (hipStream_t)stream;
   if (s->kv_dtype == GQA_F32) {
     return s->d == 64 ? dispatch_f32<64>(prm.G, s->out_dtype, grid, prm, hs)
                       : dispatch_f32<128>(prm.G, s->out_dtype, grid, prm, hs);
   }
-  if (s->kv_dtype == GQA_BF16) {
-    return s->d == 64 ? dispatch_mfma<64, false>(prm.G, s->out_dtype, grid, prm, hs)
-                      : dispatch_mfma<128, false>(prm.G, s->out_dtype, grid, prm, hs);
-  }
-  return s->d == 64 ? dispatch_mfma<64, true>(prm.G, s->out_dtype, grid, prm, hs)
-                    : dispatch_mfma<128, true>(prm.G, s->out_dtype, grid, prm, hs);
+  return dispatch_mfma_dtype<false>(s->kv_dtype, s->d, prm.G, s->out_dtype, grid, prm, hs);
+}
+
+gqa_status_t gqa_paged_shape_check(const gqa_paged_shape_t* s) {
+  if (!s) return GQA_ERR_INVALID_ARG;
+  if (s->block_size <= 0 || s->max_blocks <= 0 || s->num_blocks <= 0) return GQA_ERR_INVALID_ARG;
+  if ((long long)s->max_blocks * s->block_size >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
+  const gqa_shape_t e = dense_equivalent(s);
+  const gqa_status_t st = gqa_shape_check(&e);
+  if (st != GQA_OK) return st;
+  if (s->kv_dtype == GQA_F32) return GQA_ERR_UNSUPPORTED;  // paged caches: bf16 or fp8 only
+  const int shift = log2_exact(s->block_size);
+  if (shift < 4 || shift > 12) return GQA_ERR_UNSUPPORTED;  // 16 .. 4096 positions per page
+  if ((long long)s->max_blocks * s->B >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+size_t gqa_decode_paged_workspace_bytes(const gqa_paged_shape_t* s) {
+  if (gqa_paged_shape_check(s) != GQA_OK) return 0;
+  const gqa_shape_t e = dense_equivalent(s);
+  return plan(&e).total;
+}
+
+gqa_status_t gqa_paged_workspace_init(void* workspace, size_t workspace_bytes, const gqa_paged_shape_t* s,
+                                      void* stream) {
+  const gqa_status_t st = gqa_paged_shape_check(s);
+  if (st != GQA_OK) return st;
+  const gqa_shape_t e = dense_equivalent(s);
+  return gqa_workspace_init(workspace, workspace_bytes, &e, stream);
+}
+
+gqa_status_t gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, const int32_t* seq_lens, float scale, void* out,
+                              const gqa_paged_shape_t* s, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out || !s) return GQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16) ||
+      !aligned(seq_lens, 4) || !aligned(block_table, 4))
+    return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  const gqa_status_t st = gqa_paged_shape_check(s);
+  if (st != GQA_OK) return st;
+  const gqa_shape_t e = dense_equivalent(s);
+  const Layout lo = plan(&e);
+  if (!workspace || workspace_bytes < lo.total) return GQA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return GQA_ERR_INVALID_ARG;
+
+  gqa::Params prm = base_params(q, k_pages, v_pages, seq_lens, scale, out, &e, lo, workspace);
+  prm.block_table = block_table;
+  prm.block_shift = log2_exact(s->block_size);
+  prm.max_blocks = s->max_blocks;
+  prm.num_blocks = s->num_blocks;
+  return dispatch_mfma_dtype<true>(s->kv_dtype, s->d, prm.G, s->out_dtype, lo.workgroups, prm,
+                                   (hipStream_t)stream);
 }
 
 uint64_t gqa_kv_bytes_per_token(uint32_t layers, uint32_t kv_heads, uint32_t head_dim,

@@ -58,6 +58,10 @@ struct Params {
   int W;            // workgroups launched
   float qk_scale;   // scale * k_descale * log2(e)
   float v_descale;  // applied to the normalised output
+  // paged cache only: k and v are page pools [num_blocks][Hkv][block_size][D]; block_table is
+  // [B][max_blocks]; block_size = 1 << block_shift positions per page.
+  const int32_t* block_table;
+  int block_shift, max_blocks, num_blocks;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -427,7 +431,14 @@ __device__ void for_each_piece(const Params& p, const Range& r, Body&& body) {
 //   O[g = r][c = 16m + 4q + i], so the running max / sum of row g live in the same lanes as its
 //   outputs.
 // NT = 16-row tiles of query rows (G <= 16 * NT).
-template <int D, int NT, bool FP8, typename OutT, int NW>
+//
+// PAGED: the cache lives in pages of block_size (a power of two, at least TILE) positions, so a tile
+// never straddles two pages.  Each register set of the pipeline carries the page-table entry of the
+// tile it will receive next (two tiles on in the wave's order): the entry is loaded just ahead of
+// the set's own tile loads and moved to a scalar register when that tile is computed, after the
+// wait for the tile, so it never costs a wait of its own.  The page's buffer descriptors are built
+// per tile; a page number outside the pool yields a descriptor of zero bytes.
+template <int D, int NT, bool FP8, typename OutT, int NW, bool PAGED>
 __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(Params p) {
   constexpr int TILE = 16;
   constexpr int NTH = NW * 64;
@@ -449,7 +460,7 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
   Range rg;
   if (!find_range<TILE, NTH>(p, sh, rg)) return;
 
-  const int w = threadIdx.x / 64;
+  const int w = uniform((int)threadIdx.x / 64);  // wave index, scalar: tile addressing derives from it
   const int l = threadIdx.x % 64;
   const int q = l / 16;
   const int r = l % 16;
@@ -476,10 +487,15 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
         }
       }
     }
-    const size_t head = ((size_t)pc.b * p.Hkv + pc.j) * (size_t)p.L * ROWB;
+    const size_t head = PAGED ? 0 : ((size_t)pc.b * p.Hkv + pc.j) * (size_t)p.L * ROWB;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(p.k) + head, (uint32_t)n * ROWB);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(p.v) + head, (uint32_t)n * ROWB);
     const int mine = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;  // piece tiles w, w+NW, ...
+
+    // paged cache: this sequence's page-table row
+    __amdgpu_buffer_rsrc_t rtab = rk;
+    if constexpr (PAGED)
+      rtab = make_rsrc(p.block_table + (size_t)pc.b * p.max_blocks, (uint32_t)p.max_blocks * 4);
 
     float m_run[NT], l_run[NT];
     f32x4_t o[NT][MT];
@@ -494,25 +510,46 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
     struct Regs {
       u32x4_t k[NK];
       u32x4_t v[NV];
+      int32_t pg;  // paged cache: page-table entry of the next tile this set receives (in flight)
+      int page;    // ... the same entry once loaded (scalar)
     };
     auto tile_start = [&](int it) { return (tile0 + w + it * NW) * TILE; };
+    auto load_entry = [&](int it) {  // page-table entry of this wave's tile `it` (every lane the same)
+      const uint32_t lpage = (uint32_t)(tile_start(it) >> p.block_shift);
+      return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rtab, it < mine ? lpage * 4 : kNoTile, 0, 0);
+    };
     auto issue = [&](Regs& R, int it) {
       const bool live = it < mine;
-      const uint32_t t0 = live ? (uint32_t)tile_start(it) : 0u;
+      uint32_t t0 = live ? (uint32_t)tile_start(it) : 0u;
+      __amdgpu_buffer_rsrc_t tk = rk, tv = rv;
+      if constexpr (PAGED) {
+        if (live) {
+          const int page = R.page;
+          const int lpage = (int)(t0 >> p.block_shift);  // logical page of the tile
+          const int rows = min(1 << p.block_shift, n - (lpage << p.block_shift));
+          const uint32_t bytes = (uint32_t)page < (uint32_t)p.num_blocks ? (uint32_t)rows * ROWB : 0u;
+          const size_t pbase = (((size_t)page * p.Hkv + pc.j) << p.block_shift) * ROWB;
+          tk = make_rsrc(static_cast<const char*>(p.k) + pbase, bytes);
+          tv = make_rsrc(static_cast<const char*>(p.v) + pbase, bytes);
+          t0 &= (1u << p.block_shift) - 1;  // position within the page
+        }
+      }
+      if constexpr (PAGED) R.pg = load_entry(it + 2);
 #pragma unroll
       for (int x = 0; x < NK; ++x) {  // 16-byte column block x of this lane's quad, token row r
         const uint32_t off = (t0 + r) * ROWB + x * 64 + q * 16;
-        R.k[x] = load16(rk, live ? off : kNoTile);
+        R.k[x] = load16(tk, live ? off : kNoTile);
       }
 #pragma unroll
       for (int x = 0; x < NV; ++x) {
         const uint32_t off = t0 * ROWB + (x * 64 + l) * 16;
-        R.v[x] = load16(rv, live ? off : kNoTile);
+        R.v[x] = load16(tv, live ? off : kNoTile);
       }
     };
 
     auto compute = [&](Regs& R, int it) {
       const int t0 = tile_start(it);
+      if constexpr (PAGED) R.page = uniform(R.pg);  // loaded ahead of this tile's data
       // -- stage V (as bf16) into the wave's LDS tile, 16-byte chunks XOR-swizzled by row
 #pragma unroll
       for (int x = 0; x < NV; ++x) {
@@ -595,6 +632,10 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
 
     // ---- software pipeline: the next tile's loads are in flight while this tile is computed
     Regs A, B;
+    if constexpr (PAGED) {
+      A.page = uniform(load_entry(0));
+      B.page = uniform(load_entry(1));
+    }
     issue(A, 0);
     for (int it = 0; it < mine; it += 2) {
       issue(B, it + 1);

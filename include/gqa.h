@@ -90,6 +90,55 @@ gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* seq_lens, float scale, void* out, const gqa_shape_t* shape,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------------------
+ * Paged cache.  Serving engines keep the cache in fixed-size pages handed out on demand ("Grouped
+ * Query Attention: Why 8 KV Heads Decide Your Batch Size", section "What should you do about it?",
+ * lists paged allocation among the levers; "Grouped-Query Attention: How Sharing KV Heads Shrinks
+ * Inference Memory" cites the PagedAttention paper among its references).  The operation is the
+ * decode above over the un-paged cache: position t of sequence b is row t % block_size of physical
+ * page block_table[b][t / block_size].
+ *
+ * Memory layout (device memory; q, pages and out 16-byte aligned, tables 4-byte aligned):
+ *     q            [B, Hq, d]                              dtype q_dtype
+ *     k_pages      [num_blocks, Hkv, block_size, d]        dtype kv_dtype (bf16 or fp8-e4m3)
+ *     v_pages      [num_blocks, Hkv, block_size, d]        dtype kv_dtype
+ *     block_table  [B, max_blocks]                         int32 physical page numbers
+ *     seq_lens     [B]                                     int32 in [0, max_blocks * block_size]
+ *     out          [B, Hq, d]                              dtype out_dtype
+ * Each (page, KV head) is one contiguous block_size x d run, so whole 16-position tiles of one KV
+ * head come from one page.  Only the entries of pages that hold positions below seq_lens[b] are read;
+ * the rest of a row may hold anything.  A page number outside [0, num_blocks) in a read entry is a
+ * caller error: the kernel reads zeros for that page instead of faulting, so the output row is then
+ * meaningless but no memory outside the pools is touched.
+ */
+typedef struct {
+  int32_t B, Hq, Hkv, d;
+  int32_t block_size; /* positions per page: a power of two, 16 .. 4096 */
+  int32_t max_blocks; /* entries per block_table row; sequences hold at most max_blocks * block_size */
+  int32_t num_blocks; /* pages in each of k_pages and v_pages */
+  int32_t q_dtype, kv_dtype, out_dtype;
+  float k_descale, v_descale;
+  int32_t num_workgroups; /* as in gqa_shape_t */
+} gqa_paged_shape_t;
+
+/* Validates a paged shape: the checks of gqa_shape_check with L = max_blocks * block_size, plus the
+ * page geometry above.  f32 caches are not supported paged (GQA_ERR_UNSUPPORTED).  Host only. */
+gqa_status_t gqa_paged_shape_check(const gqa_paged_shape_t* shape);
+
+/* Workspace bytes for gqa_decode_paged (same layout as gqa_decode_workspace_bytes); 0 if invalid. */
+size_t gqa_decode_paged_workspace_bytes(const gqa_paged_shape_t* shape);
+
+/* gqa_workspace_init for a paged shape. */
+gqa_status_t gqa_paged_workspace_init(void* workspace, size_t workspace_bytes,
+                                      const gqa_paged_shape_t* shape, void* stream);
+
+/* Enqueues the paged decode on `stream`; same contract as gqa_decode otherwise (asynchronous, all
+ * host-checkable errors returned before any HIP call, seq_lens and block_table read on the device). */
+gqa_status_t gqa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                              const int32_t* block_table, const int32_t* seq_lens, float scale, void* out,
+                              const gqa_paged_shape_t* shape, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* KV-cache bytes per token: 2 (one K and one V tensor) * layers * kv_heads * head_dim * dtype_bytes
  * ("Grouped Query Attention: Why 8 KV Heads Decide Your Batch Size", section "Why does GQA decide
  * your batch size?").  Computed in 64-bit; host only. */

@@ -69,3 +69,34 @@ def decode(q, k, v, seq_lens, scale, q_dtype="f32", kv_dtype="f32", k_descale=1.
             rows.append([math.fsum(p[t] * vals[t][c] for t in range(n)) for c in range(d)])
         out.append(rows)
     return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, q_dtype="f32", kv_dtype="f32",
+                 k_descale=1.0, v_descale=1.0):
+    """Paged cache: k_pages, v_pages nested [num_blocks][Hkv][block_size][d]; block_table nested
+    [B][max_blocks].  Position t of sequence b is row t % block_size of page block_table[b][t //
+    block_size].  Gathers each sequence's rows into a dense nested cache and applies ``decode``."""
+    B = len(q)
+    Hkv = len(k_pages[0]) if k_pages else 1
+    bs = len(k_pages[0][0]) if k_pages else 1
+    d = len(q[0][0]) if B else 0
+    L = max([int(n) for n in seq_lens] + [1])
+    kd, vd = [], []
+    for b in range(B):
+        n = int(seq_lens[b])
+        kb, vb = [], []
+        for j in range(Hkv):
+            rows_k, rows_v = [], []
+            for t in range(L):
+                if t < n:
+                    page = int(block_table[b][t // bs])
+                    rows_k.append(list(k_pages[page][j][t % bs]))
+                    rows_v.append(list(v_pages[page][j][t % bs]))
+                else:
+                    rows_k.append([0] * d)
+                    rows_v.append([0] * d)
+            kb.append(rows_k)
+            vb.append(rows_v)
+        kd.append(kb)
+        vd.append(vb)
+    return decode(q, kd, vd, seq_lens, scale, q_dtype, kv_dtype, k_descale, v_descale)

@@ -23,8 +23,18 @@
  *     ("Grouped-Query Attention: How Sharing KV Heads Shrinks Inference Memory", section "FP8 KV cache:
  *     the other factor of two".)  The 8-bit format is OCP e4m3fn, decoded here from its definition.
  *
+ *   - Paged cache ("Grouped Query Attention: Why 8 KV Heads Decide Your Batch Size", section "What
+ *     should you do about it?", names paged allocation as a serving lever, with the PagedAttention
+ *     paper among the references of "Grouped-Query Attention: How Sharing KV Heads Shrinks Inference
+ *     Memory"): the cache positions of a sequence live in fixed-size pages of block_size positions;
+ *     logical page t / block_size of sequence b is physical page block_table[b][t / block_size], and
+ *     position t sits at row t % block_size of it.  Pages are laid out [num_blocks][Hkv][block_size][d].
+ *     The attention itself is the dense one over the un-paged cache.
+ *
  * Readings where the pages are silent: seq_len 0 yields an all-zero output row; seq_len outside [0, L]
- * is an error (return code 2); the output is returned in fp64 so that the caller's comparison includes
+ * is an error (return code 2); a page-table entry of a live page outside [0, num_blocks) is an error
+ * (return code 3) while entries of pages past a sequence's length are never read; the output is
+ * returned in fp64 so that the caller's comparison includes
  * whatever rounding the device path applies.
  *
  * Every input element is decoded exactly to double; all accumulation is double, in plain index order.
@@ -98,15 +108,34 @@ typedef struct {
   double k_descale, v_descale, scale;
   const int32_t* seq_lens;
   int B, Hq, Hkv, L, d;
+  /* paged cache (block_table == NULL: dense [B][Hkv][L][d]) */
+  const int32_t* block_table; /* [B][max_blocks] */
+  int block_size, max_blocks, num_blocks;
 } problem_t;
 
 static int check(const problem_t* p) {
   if (p->B < 0 || p->Hq <= 0 || p->Hkv <= 0 || p->L < 0 || p->d <= 0) return 1;
   if (p->Hq % p->Hkv != 0) return 1;
   if (!elem_size(p->q_dtype) || !elem_size(p->kv_dtype)) return 1;
+  if (p->block_table && (p->block_size <= 0 || p->max_blocks < 0 || p->num_blocks < 0)) return 1;
   for (int b = 0; b < p->B; ++b)
     if (p->seq_lens[b] < 0 || p->seq_lens[b] > p->L) return 2;
+  if (p->block_table)
+    for (int b = 0; b < p->B; ++b) {
+      const int live = (p->seq_lens[b] + p->block_size - 1) / p->block_size;
+      for (int i = 0; i < live; ++i) {
+        const int32_t pg = p->block_table[(size_t)b * p->max_blocks + i];
+        if (pg < 0 || pg >= p->num_blocks) return 3;
+      }
+    }
   return 0;
+}
+
+/* Element index of element 0 of cache row (b, j, t). */
+static size_t row_index(const problem_t* p, int b, int j, int t) {
+  if (!p->block_table) return (((size_t)b * p->Hkv + j) * (size_t)p->L + (size_t)t) * p->d;
+  const size_t page = (size_t)p->block_table[(size_t)b * p->max_blocks + t / p->block_size];
+  return ((page * p->Hkv + j) * (size_t)p->block_size + (size_t)(t % p->block_size)) * p->d;
 }
 
 /* Softmax weights of query head (b, h) over its n cached tokens, written to w[0..n).  Returns n. */
@@ -115,14 +144,14 @@ static int head_weights(const problem_t* p, int b, int h, double* w) {
   const int j = h / G; /* contiguous grouping */
   const int n = p->seq_lens[b];
   const size_t qbase = ((size_t)b * p->Hq + h) * p->d;
-  const size_t kbase = ((size_t)b * p->Hkv + j) * (size_t)p->L * p->d;
   if (n == 0) return 0;
   double m = -INFINITY;
   for (int t = 0; t < n; ++t) {
+    const size_t krow = row_index(p, b, j, t);
     double dot = 0.0;
     for (int c = 0; c < p->d; ++c)
       dot += load_elem(p->q, p->q_dtype, qbase + c) *
-             (load_elem(p->k, p->kv_dtype, kbase + (size_t)t * p->d + c) * p->k_descale);
+             (load_elem(p->k, p->kv_dtype, krow + c) * p->k_descale);
     w[t] = dot * p->scale;
     if (w[t] > m) m = w[t];
   }
@@ -138,12 +167,11 @@ static int head_weights(const problem_t* p, int b, int h, double* w) {
 static void head_output(const problem_t* p, int b, int h, double* w, double* out_row) {
   const int G = p->Hq / p->Hkv;
   const int j = h / G;
-  const size_t vbase = ((size_t)b * p->Hkv + j) * (size_t)p->L * p->d;
   const int n = head_weights(p, b, h, w);
   for (int c = 0; c < p->d; ++c) {
     double acc = 0.0;
     for (int t = 0; t < n; ++t)
-      acc += w[t] * (load_elem(p->v, p->kv_dtype, vbase + (size_t)t * p->d + c) * p->v_descale);
+      acc += w[t] * (load_elem(p->v, p->kv_dtype, row_index(p, b, j, t) + c) * p->v_descale);
     out_row[c] = acc; /* n == 0 leaves the row at zero */
   }
 }
@@ -152,7 +180,8 @@ static void head_output(const problem_t* p, int b, int h, double* w, double* out
   problem_t p;                                                                                  \
   p.q = q; p.k = k; p.v = v; p.q_dtype = q_dtype; p.kv_dtype = kv_dtype;                        \
   p.k_descale = k_descale; p.v_descale = v_descale; p.scale = scale; p.seq_lens = seq_lens;     \
-  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.d = d;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.L = L; p.d = d;                                          \
+  p.block_table = NULL; p.block_size = 0; p.max_blocks = 0; p.num_blocks = 0;
 
 /* Full decode: out[B, Hq, d] (fp64).  w_scratch must hold L doubles.  Returns 0, 1 (bad shape or
  * dtype) or 2 (a seq_len outside [0, L]). */
@@ -192,4 +221,36 @@ int gqa_oracle_weights(const void* q, int q_dtype, const void* k, const void* v,
   if (rc) return -rc;
   if (b < 0 || b >= B || h < 0 || h >= Hq) return -1;
   return head_weights(&p, b, h, w);
+}
+
+/* Paged cache: k_pages, v_pages are [num_blocks][Hkv][block_size][d]; block_table is [B][max_blocks];
+ * sequences hold at most L = max_blocks * block_size positions.  rows == NULL computes every (b, h) into
+ * out[B, Hq, d]; otherwise only the nrows listed (b, h) pairs into out[nrows, d].  w_scratch holds L
+ * doubles.  Returns 0, 1 (bad shape or dtype), 2 (a seq_len outside [0, L]) or 3 (a live page-table
+ * entry outside [0, num_blocks)). */
+int gqa_oracle_decode_paged(const void* q, int q_dtype, const void* k_pages, const void* v_pages,
+                            int kv_dtype, double k_descale, double v_descale,
+                            const int32_t* block_table, const int32_t* seq_lens, double scale, int B,
+                            int Hq, int Hkv, int block_size, int max_blocks, int num_blocks, int d,
+                            const int32_t* rows, int nrows, double* w_scratch, double* out) {
+  problem_t p;
+  p.q = q; p.k = k_pages; p.v = v_pages; p.q_dtype = q_dtype; p.kv_dtype = kv_dtype;
+  p.k_descale = k_descale; p.v_descale = v_descale; p.scale = scale; p.seq_lens = seq_lens;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.d = d;
+  p.block_table = block_table; p.block_size = block_size; p.max_blocks = max_blocks;
+  p.num_blocks = num_blocks;
+  p.L = (block_size > 0 && max_blocks >= 0) ? block_size * max_blocks : -1;
+  int rc = check(&p);
+  if (rc) return rc;
+  if (!rows) {
+    for (int b = 0; b < B; ++b)
+      for (int h = 0; h < Hq; ++h) head_output(&p, b, h, w_scratch, out + ((size_t)b * Hq + h) * d);
+    return 0;
+  }
+  for (int r = 0; r < nrows; ++r) {
+    int b = rows[2 * r], h = rows[2 * r + 1];
+    if (b < 0 || b >= B || h < 0 || h >= Hq) return 1;
+    head_output(&p, b, h, w_scratch, out + (size_t)r * d);
+  }
+  return 0;
 }

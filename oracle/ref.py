@@ -32,6 +32,10 @@ def lib():
         L.gqa_oracle_decode_rows.restype = c_int
         L.gqa_oracle_weights.argtypes = common + [c_int, c_int, c_void]
         L.gqa_oracle_weights.restype = c_int
+        L.gqa_oracle_decode_paged.argtypes = [c_void, c_int, c_void, c_void, c_int, c_dbl, c_dbl, c_void,
+                                              c_void, c_dbl, c_int, c_int, c_int, c_int, c_int, c_int,
+                                              c_int, c_void, c_int, c_void, c_void]
+        L.gqa_oracle_decode_paged.restype = c_int
         L.gqa_oracle_kv_bytes_per_token.argtypes = [ctypes.c_uint64] * 4
         L.gqa_oracle_kv_bytes_per_token.restype = ctypes.c_uint64
         L.gqa_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -79,6 +83,8 @@ def _raise(rc):
         raise ValueError("oracle: invalid shape or dtype")
     if rc == 2:
         raise ValueError("oracle: a seq_len lies outside [0, L]")
+    if rc == 3:
+        raise ValueError("oracle: a live page-table entry lies outside [0, num_blocks)")
     if rc:
         raise RuntimeError(f"oracle: error {rc}")
 
@@ -119,6 +125,42 @@ def weights(q, k, v, seq_lens, scale, b, h, q_dtype="f32", kv_dtype="f32", k_des
         _raise(-n)
     del keep
     return w[:n].copy()
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, rows=None, q_dtype="bf16",
+                 kv_dtype="bf16", k_descale=1.0, v_descale=1.0):
+    """Decode over a paged cache.  k_pages, v_pages: [num_blocks, Hkv, block_size, d]; block_table:
+    [B, max_blocks] int32.  Returns out[B, Hq, d] (rows None) or [len(rows), d], float64."""
+    qa = raw(q, q_dtype)
+    ka, va = raw(k_pages, kv_dtype), raw(v_pages, kv_dtype)
+    if qa.ndim != 3 or ka.ndim != 4 or va.shape != ka.shape:
+        raise ValueError("q must be [B,Hq,d]; pages [num_blocks,Hkv,block_size,d]")
+    B, Hq, d = qa.shape
+    num_blocks, Hkv, block_size, dk = ka.shape
+    if dk != d:
+        raise ValueError("head_dim mismatch between q and the pages")
+    bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    if bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks]")
+    max_blocks = bt.shape[1]
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32).reshape(-1))
+    if sl.shape[0] != B:
+        raise ValueError("seq_lens must have B entries")
+    L = block_size * max_blocks
+    if rows is None:
+        r, nrows, out = None, 0, np.zeros((B, Hq, d), dtype=np.float64)
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+        nrows, out = r.shape[0], np.zeros((r.shape[0], d), dtype=np.float64)
+    w = np.zeros(max(L, 1), dtype=np.float64)
+    rc = lib().gqa_oracle_decode_paged(
+        qa.ctypes.data, DTYPES[q_dtype], ka.ctypes.data, va.ctypes.data, DTYPES[kv_dtype],
+        float(k_descale), float(v_descale), bt.ctypes.data, sl.ctypes.data, float(scale), B, Hq, Hkv,
+        block_size, max_blocks, num_blocks, d, None if r is None else r.ctypes.data, nrows,
+        w.ctypes.data, out.ctypes.data)
+    _raise(rc)
+    del qa, ka, va, bt, sl
+    return out
 
 
 def kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes=2):

@@ -138,3 +138,41 @@ def test_python_binding_validates_tensors():
         gqa.decode(q, k, k[:, :1], sl)               # K and V shapes differ
     with pytest.raises(ValueError):
         gqa.decode(q, k, k, sl.long())               # seq_lens dtype
+
+
+def _paged(**kw):
+    base = dict(B=2, Hq=8, Hkv=2, d=128, block_size=16, max_blocks=64, num_blocks=100,
+                q_dtype=gqa.BF16, kv_dtype=gqa.BF16)
+    base.update(kw)
+    return gqa.make_paged_shape(**base)
+
+
+def test_paged_shapes():
+    assert gqa.shape_check(_paged()) == 0
+    assert gqa.shape_check(_paged(block_size=4096, max_blocks=2, kv_dtype=gqa.FP8_E4M3)) == 0
+    for kw, code in [(dict(block_size=0), 1), (dict(max_blocks=0), 1), (dict(num_blocks=-1), 1),
+                     (dict(Hq=6, Hkv=4), 1), (dict(block_size=8), 2), (dict(block_size=48), 2),
+                     (dict(block_size=8192), 2), (dict(q_dtype=gqa.F32, kv_dtype=gqa.F32), 2),
+                     (dict(max_blocks=1 << 28), 2), (dict(d=96), 2)]:
+        assert gqa.shape_check(_paged(**kw)) == code, kw
+        assert gqa.workspace_bytes(_paged(**kw)) == 0
+    # the paged workspace is the dense one of L = max_blocks * block_size
+    dense = gqa.make_shape(2, 8, 2, 64 * 16, 128, gqa.BF16, gqa.BF16)
+    assert gqa.workspace_bytes(_paged()) == gqa.workspace_bytes(dense)
+
+
+def test_paged_decode_rejects_before_any_hip_call():
+    good = ctypes.c_void_p(1 << 20)
+    s = _paged()
+
+    def call(shape=s, wsb=1 << 30, **over):
+        a = dict(q=good, k=good, v=good, t=good, sl=good, out=good, ws=good)
+        a.update(over)
+        return gqa.lib.gqa_decode_paged(a["q"], a["k"], a["v"], a["t"], a["sl"], 0.1, a["out"],
+                                        ctypes.byref(shape), a["ws"], wsb, None)
+
+    assert call(t=None) == 1
+    assert call(t=ctypes.c_void_p((1 << 20) + 2)) == 1      # table misaligned
+    assert call(k=ctypes.c_void_p((1 << 20) + 8)) == 1
+    assert call(shape=_paged(block_size=24)) == 2
+    assert call(wsb=16) == 3

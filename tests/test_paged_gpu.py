@@ -1,0 +1,126 @@
+"""GPU parity of the paged-cache decode (gqa_decode_paged) against the fp64 oracle, through the C ABI.
+
+Same gates as the dense path.  The pools are filled by a seeded random page placement; unused pages,
+page rows past a sequence's end and dead table entries hold NaN or wild page numbers, so reading any
+of them would show.
+"""
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_attention_04_amd as gqa
+import workloads
+from oracle import ref
+from tests.test_parity_gpu import ABS_GATE, DEV, TORCH, _sample_rows, compare, say
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [("bf16", "bf16"), ("bf16", "fp8_e4m3")]
+
+
+def run_paged(case, pg, out_dtype=None, workgroups=0, table=None):
+    t = (pg["block_table"] if table is None else table).to(DEV)
+    od = TORCH[out_dtype or case["out_dtype"]]
+    out = gqa.decode_paged(case["q"].to(DEV), pg["k_pages"].to(DEV), pg["v_pages"].to(DEV), t,
+                           case["seq_lens"].to(DEV), case["scale"], out_dtype=od,
+                           k_descale=case["k_descale"], v_descale=case["v_descale"],
+                           num_workgroups=workgroups)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_paged(case, pg, rows=None, table=None):
+    return ref.decode_paged(case["q"], pg["k_pages"], pg["v_pages"],
+                            (pg["block_table"] if table is None else table).numpy(),
+                            case["seq_lens"].numpy(), case["scale"], rows, case["q_dtype"],
+                            case["kv_dtype"], case["k_descale"], case["v_descale"])
+
+
+PAGED_SMALL = [
+    # (B, Hq, Hkv, d, L, seq_lens, block_size, workgroups)
+    (3, 16, 4, 128, 1100, (1100, 777, 33), 16, 256),
+    (2, 8, 2, 64, 700, (700, 1), 32, 256),
+    (2, 8, 8, 128, 600, (513, 600), 64, 0),       # G = 1
+    (2, 32, 1, 128, 520, (520, 257), 16, 256),    # G = 32
+    (1, 10, 2, 128, 900, (899,), 128, 7),         # G = 5
+    (2, 16, 2, 128, 5000, (5000, 4111), 16, 1),   # one workgroup: > 64 tiles per wave and piece
+    (2, 16, 2, 128, 9000, (9000, 8999), 256, 3),  # three page windows per wave and piece
+    (1, 8, 1, 64, 4096, (4096,), 4096, 2),        # one page per sequence
+    (3, 8, 2, 128, 300, (0, 300, 17), 16, 256),   # an empty sequence
+]
+
+
+@pytest.mark.parametrize("qd,kd", DTYPES)
+@pytest.mark.parametrize("cfg", PAGED_SMALL, ids=lambda c: f"B{c[0]}Hq{c[1]}Hkv{c[2]}d{c[3]}L{c[4]}bs{c[6]}")
+def test_paged_small_parity(cfg, qd, kd):
+    B, Hq, Hkv, d, L, sl, bs, wg = cfg
+    say(f"paged parity {cfg} q={qd} kv={kd}")
+    case = workloads.make_case(B, Hq, Hkv, d, L, qd, kd, seq_lens=sl, seed=hash(cfg) % 10000)
+    pg = workloads.paginate(case, bs, seed=5, spare_pages=2)
+    want = oracle_paged(case, pg)
+    compare(run_paged(case, pg, workgroups=wg), want, kd, "native out")
+    compare(run_paged(case, pg, out_dtype="f32", workgroups=wg), want, kd, "f32 out")
+
+
+@pytest.mark.parametrize("qd,kd", DTYPES)
+@pytest.mark.parametrize("bs,wg", [(16, 0), (64, 5), (256, 1)])
+def test_paged_is_bitwise_the_dense_result(qd, kd, bs, wg):
+    """Same bytes, same work split: the paged kernel must reproduce the dense kernel exactly."""
+    say(f"paged == dense bitwise bs={bs} wg={wg} q={qd} kv={kd}")
+    case = workloads.make_case(4, 32, 8, 128, 3000, qd, kd, seq_range=(1, 3000), seed=41)
+    pg = workloads.paginate(case, bs, seed=6, spare_pages=4)
+    dense = gqa.decode(case["q"].to(DEV), case["k"].to(DEV), case["v"].to(DEV),
+                       case["seq_lens"].to(DEV), case["scale"], num_workgroups=wg)
+    paged = run_paged(case, pg, workgroups=wg)
+    assert torch.equal(dense, paged)
+
+
+def test_paged_ignores_dead_entries_spare_pages_and_page_tails():
+    say("paged: dead entries, spare pages and page tails are never read")
+    case = workloads.make_case(3, 16, 4, 128, 1000, "bf16", "bf16", seq_lens=(1000, 37, 500), seed=42)
+    clean = run_paged(case, workloads.paginate(case, 64, seed=7)).cpu()
+    k, v = case["k"].clone(), case["v"].clone()
+    for b, n in enumerate(case["seq_lens"].tolist()):
+        k[b, :, n:] = float("nan")               # rows past the end of the last live page
+        v[b, :, n:] = float("nan")
+    poisoned = dict(case, k=k, v=v)
+    for dead in (10**9, -7):
+        pg = workloads.paginate(poisoned, 64, seed=7, spare_pages=6, dead_entry=dead)
+        got = run_paged(poisoned, pg).cpu()
+        assert torch.isfinite(got.float()).all()
+        assert torch.equal(got, clean), dead
+
+
+def test_paged_out_of_pool_entry_reads_zeros():
+    """A live entry outside [0, num_blocks) is a caller error that the kernel's own bounds check turns
+    into a page of zeros (no access outside the pools)."""
+    say("paged: out-of-pool live entry reads a zero page")
+    case = workloads.make_case(2, 8, 2, 128, 256, "bf16", "bf16", seq_lens=(256, 200), seed=43)
+    pg = workloads.paginate(case, 16, seed=8)
+    bad = pg["block_table"].clone()
+    bad[1, 3] = pg["num_blocks"] + 12345
+    got = run_paged(case, pg, out_dtype="f32", table=bad)
+    # expected: the same table pointing at an added all-zero page
+    zk = torch.zeros((1,) + tuple(pg["k_pages"].shape[1:]), dtype=pg["k_pages"].dtype)
+    zpg = dict(pg, k_pages=torch.cat([pg["k_pages"], zk]), v_pages=torch.cat([pg["v_pages"], zk]))
+    ztab = pg["block_table"].clone()
+    ztab[1, 3] = pg["num_blocks"]
+    compare(got, oracle_paged(case, zpg, table=ztab), "bf16", "zero page")
+
+
+@pytest.mark.parametrize("wid,bs", [(3, 16), (5, 64), (2, 32)])
+def test_paged_workload_parity(wid, bs):
+    """Full-size workloads in paged form, library's workgroup count, sampled rows vs the oracle."""
+    w = workloads.WORKLOADS[wid]
+    say(f"paged workload {wid} block_size {bs}: {w.name}")
+    case = workloads.make(wid)
+    pg = workloads.paginate(case, bs, seed=9, spare_pages=8)
+    got = run_paged(case, pg).cpu()
+    rows = _sample_rows(case)
+    want = oracle_paged(case, pg, rows=rows)
+    sel = torch.stack([got[b, h] for b, h in rows])
+    bad = [rows[i] for i in range(len(rows))
+           if not np.abs(sel[i].double().numpy() - want[i]).max() <= ABS_GATE[w.kv_dtype]]
+    if bad:
+        say(f"  rows off the oracle: {bad}")
+    compare(sel, want, w.kv_dtype, f"paged workload {wid} {len(rows)} rows")

@@ -9,6 +9,8 @@ are random), then q, K and V as float32 standard normals; the values are then ca
 round-to-nearest-even to the storage dtype.  The fp8-e4m3fn cache is clipped to [-4, 4] first and
 stored with per-tensor descale 1.0.  Cache positions at or beyond a sequence's length hold the same
 normal draws and are never read by a correct kernel.
+
+Paged variants (``paginate``) move the same bytes into page pools placed by a seeded permutation.
 """
 import math
 from dataclasses import dataclass, field
@@ -91,6 +93,54 @@ def make_case(B: int, Hq: int, Hkv: int, d: int, L: int, q_dtype: str = "bf16",
         "q_dtype": q_dtype, "kv_dtype": kv_dtype, "out_dtype": q_dtype,
         "B": B, "Hq": Hq, "Hkv": Hkv, "d": d, "L": L,
     }
+
+
+POISON_BITS = {"f32": 0x7FC00000, "bf16": 0x7FC0, "fp8_e4m3": 0x7F}   # a NaN in each storage format
+
+
+def poison_like(shape, dtype: str) -> torch.Tensor:
+    """A tensor of the storage dtype whose every element is NaN (never read by a correct kernel)."""
+    if dtype == "f32":
+        return torch.full(shape, POISON_BITS["f32"], dtype=torch.int32).view(torch.float32)
+    if dtype == "bf16":
+        return torch.full(shape, POISON_BITS["bf16"], dtype=torch.int16).view(torch.bfloat16)
+    return torch.full(shape, POISON_BITS["fp8_e4m3"], dtype=torch.uint8).view(torch.float8_e4m3fn)
+
+
+def paginate(case: dict, block_size: int, seed: int = 0, spare_pages: int = 0,
+             dead_entry: int = -1) -> dict:
+    """Copy a dense case's cache into page pools with a seeded random page placement.
+
+    Sequence b needs ceil(seq_lens[b] / block_size) pages; those pages, plus spare_pages unused
+    ones, are placed at the positions of a random permutation of the pool.  Pools are
+    [num_blocks, Hkv, block_size, d]; position t of sequence b goes to row t % block_size of page
+    block_table[b, t // block_size].  Page rows past the dense cache's length, and the spare pages,
+    hold NaN.  Table entries of pages a sequence does not use hold dead_entry.  Adds k_pages, v_pages,
+    block_table (int32 [B, max_blocks]), block_size and num_blocks to a copy of the case."""
+    k, v, sl = case["k"], case["v"], case["seq_lens"]
+    B, Hkv, L, d = k.shape
+    dt = case["kv_dtype"]
+    max_blocks = -(-L // block_size)
+    live = [-(-int(n) // block_size) for n in sl.tolist()]
+    num_blocks = sum(live) + spare_pages
+    g = torch.Generator().manual_seed(int(seed))
+    perm = torch.randperm(num_blocks, generator=g).tolist()
+    kp = poison_like((num_blocks, Hkv, block_size, d), dt)
+    vp = poison_like((num_blocks, Hkv, block_size, d), dt)
+    table = torch.full((B, max_blocks), int(dead_entry), dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        for i in range(live[b]):
+            page = perm[nxt]
+            nxt += 1
+            table[b, i] = page
+            lo, hi = i * block_size, min((i + 1) * block_size, L)
+            kp[page, :, : hi - lo] = k[b, :, lo:hi]
+            vp[page, :, : hi - lo] = v[b, :, lo:hi]
+    out = dict(case)
+    out.update(k_pages=kp, v_pages=vp, block_table=table, block_size=block_size,
+               num_blocks=num_blocks)
+    return out
 
 
 def make(wid, seed: Optional[int] = None) -> dict:
