@@ -25,7 +25,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV GB/s and % HBM roofline for GQA decode (Hq=64,Hkv=8,d=128,bf16)"
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gqa_decode_llama70b_traffic.md")
+# rocprofv3 counter summaries of the 70B-shaped layer, keyed by page size (0 = dense cache)
+TRAFFIC_SUMMARY = {0: os.path.join(ROOT, "profiles", "gqa_decode_llama70b_traffic.md"),
+                   16: os.path.join(ROOT, "profiles", "gqa_decode_paged16_llama70b_traffic.md")}
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_attention_04_amd", "csrc", f)
                   for f in ("gqa_kernels.h", "gqa_api.hip")]
 
@@ -42,12 +44,13 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(wid, workgroups):
+def recorded_traffic(wid, workgroups, paged=0):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on this
-    workload and launch configuration with the kernel sources as they are now; otherwise None."""
-    if wid != 3 or workgroups != 0 or not os.path.exists(TRAFFIC_SUMMARY):
+    workload, layout and launch configuration with the kernel sources as they are now; else None."""
+    path = TRAFFIC_SUMMARY.get(paged)
+    if wid != 3 or workgroups != 0 or path is None or not os.path.exists(path):
         return None
-    text = open(TRAFFIC_SUMMARY).read()
+    text = open(path).read()
     src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not src or not val or src.group(1) != kernel_source_hash():
@@ -211,7 +214,7 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {args.calib_copy_mib} MiB done")
 
-    traffic = None if paged else recorded_traffic(wid, args.workgroups)
+    traffic = recorded_traffic(wid, args.workgroups, args.paged)
     layout = f"paged, {args.paged} positions per page, random page placement" if paged else "dense"
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
