@@ -7,7 +7,9 @@ sum_b seq_lens[b] * Hkv * 2 * d * 2 (one K and one V row per cached token and KV
 copies of the cache are rotated so that no step finds its cache in the 256 MB last-level cache.
 
 With --paged BS the same workload is laid out in pages of BS positions placed by a seeded random
-permutation (gqa_decode_paged); the KV bytes counted are the same.
+permutation (gqa_decode_paged); the KV bytes counted are the same.  With --append a step first writes
+the new token's K and V rows (bf16, converted to the cache format: fp8 caches quantise) at position
+seq_lens[b] - 1 of every sequence, then decodes; the KV bytes counted are the same.
 
 Prints one JSON line on stdout (diagnostics go to stderr).
 """
@@ -89,6 +91,8 @@ def main():
     ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4-mha, 4-gqa, 4-mqa, 5)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated (0 = enough for 2 GiB)")
     ap.add_argument("--workgroups", type=int, default=0, help="workgroups (0 = library choice)")
+    ap.add_argument("--append", action="store_true",
+                    help="each step appends the new token's K/V rows before the decode")
     ap.add_argument("--paged", type=int, default=0, metavar="BS",
                     help="lay the cache out in pages of BS positions (0 = dense cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -149,7 +153,24 @@ def main():
     vptr = [t.data_ptr() for t in vs]
     scale = float(case["scale"])
 
+    if args.append:
+        g = torch.Generator().manual_seed(w.seed + 200)
+        k_new = torch.randn(w.B, w.Hkv, w.d, generator=g).to(torch.bfloat16).to(dev)
+        v_new = torch.randn(w.B, w.Hkv, w.d, generator=g).to(torch.bfloat16).to(dev)
+        positions = (sl - 1).clamp(min=-1).to(torch.int32).to(dev)
+        ashape = shape
+
     def step(i):
+        if args.append:
+            if paged:
+                rc = gqa.lib.gqa_append_kv_paged(k_new.data_ptr(), v_new.data_ptr(), gqa.BF16, kptr[i % copies],
+                                                 vptr[i % copies], table.data_ptr(), ctypes.byref(ashape),
+                                                 positions.data_ptr(), None, sh)
+            else:
+                rc = gqa.lib.gqa_append_kv(k_new.data_ptr(), v_new.data_ptr(), gqa.BF16, kptr[i % copies],
+                                           vptr[i % copies], ctypes.byref(ashape), positions.data_ptr(), None, sh)
+            if rc:
+                raise RuntimeError(gqa.status_string(rc))
         if paged:
             rc = gqa.lib.gqa_decode_paged(q.data_ptr(), kptr[i % copies], vptr[i % copies], table.data_ptr(),
                                           seq.data_ptr(), scale, out.data_ptr(), shape_ref, ws.data_ptr(),
@@ -216,12 +237,16 @@ def main():
 
     traffic = recorded_traffic(wid, args.workgroups, args.paged)
     layout = f"paged, {args.paged} positions per page, random page placement" if paged else "dense"
+    if args.append:
+        layout += "; each step appends the new token's K/V (bf16 rows) then decodes"
+        traffic = None
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.kv_dtype, "data": "synthetic",
-        "config": {"workload": w.name + (f" paged bs{args.paged}" if paged else ""), "cache_layout": layout,
+        "config": {"workload": w.name + (f" paged bs{args.paged}" if paged else "") + (" append+decode" if args.append else ""),
+                   "cache_layout": layout,
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L,
                    "seq_lens": f"sum {int(sl.sum())} (min {int(sl.min())}, max {int(sl.max())})",
                    "kv_bytes_per_step": kv_bytes, "cache_copies": copies,

@@ -51,7 +51,7 @@ class PagedShape(ctypes.Structure):
 
 EXPORTS = ["gqa_shape_check", "gqa_decode_workspace_bytes", "gqa_workspace_init", "gqa_decode",
            "gqa_paged_shape_check", "gqa_decode_paged_workspace_bytes", "gqa_paged_workspace_init",
-           "gqa_decode_paged", "gqa_kv_bytes_per_token", "gqa_validate_seq_lens", "gqa_stream_read",
+           "gqa_decode_paged", "gqa_append_kv", "gqa_append_kv_paged", "gqa_kv_bytes_per_token", "gqa_validate_seq_lens", "gqa_stream_read",
            "gqa_stream_read_sink_words", "gqa_status_string"]
 
 
@@ -78,6 +78,10 @@ def _load():
     lib.gqa_paged_workspace_init.restype = ctypes.c_int
     lib.gqa_decode_paged.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, pP, vp, sz, vp]
     lib.gqa_decode_paged.restype = ctypes.c_int
+    lib.gqa_append_kv.argtypes = [vp, vp, i32, vp, vp, pS, vp, vp, vp]
+    lib.gqa_append_kv.restype = ctypes.c_int
+    lib.gqa_append_kv_paged.argtypes = [vp, vp, i32, vp, vp, vp, pP, vp, vp, vp]
+    lib.gqa_append_kv_paged.restype = ctypes.c_int
     lib.gqa_kv_bytes_per_token.argtypes = [ctypes.c_uint32] * 4
     lib.gqa_kv_bytes_per_token.restype = ctypes.c_uint64
     lib.gqa_validate_seq_lens.argtypes = [vp, i32, i32, vp, vp]
@@ -245,6 +249,57 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=Non
                                     out.data_ptr(), ctypes.byref(shape), ws.data_ptr(), ws.numel(),
                                     _stream_handle(dev)))
     return out
+
+
+def _check_append(k_new, v_new, positions, tensors, B, Hkv, d):
+    if k_new.shape != (B, Hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [B, Hkv, d] matching the cache")
+    if k_new.dtype not in (torch.float32, torch.bfloat16) or v_new.dtype != k_new.dtype:
+        raise TypeError("new rows must both be float32 or both bfloat16")
+    if positions.dtype != torch.int32 or positions.shape != (B,):
+        raise ValueError("positions must be an int32 tensor of shape [B]")
+    dev = k_new.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must live on one CUDA (HIP) device")
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous")
+    return dev
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, positions, *, k_descale=1.0, v_descale=1.0, skipped=None):
+    """Writes row (b, j) of k_new / v_new [B,Hkv,d] into the dense caches [B,Hkv,L,d] at position
+    positions[b] (int32 [B]; negative = skip), converted to the cache dtype (fp8: code of x / descale).
+    Positions past the cache add one to skipped (an int32 [1] device tensor) if given."""
+    B, Hkv, L, d = k_cache.shape
+    tensors = [k_new, v_new, k_cache, v_cache, positions] + ([skipped] if skipped is not None else [])
+    dev = _check_append(k_new, v_new, positions, tensors, B, Hkv, d)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    q_code = F32 if k_cache.dtype == torch.float32 else BF16
+    shape = make_shape(B, Hkv, Hkv, L, d, q_code, _CODE[k_cache.dtype], q_code, k_descale, v_descale)
+    with torch.cuda.device(dev):
+        _check(lib.gqa_append_kv(k_new.data_ptr(), v_new.data_ptr(), _CODE[k_new.dtype], k_cache.data_ptr(),
+                                 v_cache.data_ptr(), ctypes.byref(shape), positions.data_ptr(),
+                                 None if skipped is None else skipped.data_ptr(), _stream_handle(dev)))
+
+
+def append_kv_paged(k_new, v_new, k_pages, v_pages, block_table, positions, *, k_descale=1.0, v_descale=1.0,
+                    skipped=None):
+    """append_kv for a paged cache: pages [num_blocks,Hkv,block_size,d], block_table [B,max_blocks]."""
+    num_blocks, Hkv, block_size, d = k_pages.shape
+    B = positions.shape[0]
+    tensors = [k_new, v_new, k_pages, v_pages, block_table, positions] + ([skipped] if skipped is not None else [])
+    dev = _check_append(k_new, v_new, positions, tensors, B, Hkv, d)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be an int32 tensor of shape [B, max_blocks]")
+    q_code = BF16
+    shape = make_paged_shape(B, Hkv, Hkv, d, block_size, block_table.shape[1], num_blocks, q_code,
+                             _CODE[k_pages.dtype], q_code, k_descale, v_descale)
+    with torch.cuda.device(dev):
+        _check(lib.gqa_append_kv_paged(k_new.data_ptr(), v_new.data_ptr(), _CODE[k_new.dtype],
+                                       k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                       ctypes.byref(shape), positions.data_ptr(),
+                                       None if skipped is None else skipped.data_ptr(), _stream_handle(dev)))
 
 
 def validate_seq_lens(seq_lens, L) -> int:

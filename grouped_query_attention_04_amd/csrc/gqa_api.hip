@@ -124,6 +124,27 @@ gqa::Params base_params(const void* q, const void* k, const void* v, const int32
   return prm;
 }
 
+template <int D, typename InT, bool PAGED>
+gqa_status_t dispatch_append_kv(int kv_dtype, int B, const gqa::AppendParams& ap, hipStream_t st) {
+  if (kv_dtype == GQA_F32)
+    hipLaunchKernelGGL((gqa::append_kv_kernel<D, InT, 0, PAGED>), dim3(B), dim3(256), 0, st, ap);
+  else if (kv_dtype == GQA_BF16)
+    hipLaunchKernelGGL((gqa::append_kv_kernel<D, InT, 1, PAGED>), dim3(B), dim3(256), 0, st, ap);
+  else
+    hipLaunchKernelGGL((gqa::append_kv_kernel<D, InT, 2, PAGED>), dim3(B), dim3(256), 0, st, ap);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+template <bool PAGED>
+gqa_status_t launch_append(int new_dtype, int kv_dtype, int d, int B, const gqa::AppendParams& ap,
+                           hipStream_t st) {
+  if (new_dtype == GQA_F32)
+    return d == 64 ? dispatch_append_kv<64, float, PAGED>(kv_dtype, B, ap, st)
+                   : dispatch_append_kv<128, float, PAGED>(kv_dtype, B, ap, st);
+  return d == 64 ? dispatch_append_kv<64, uint16_t, PAGED>(kv_dtype, B, ap, st)
+                 : dispatch_append_kv<128, uint16_t, PAGED>(kv_dtype, B, ap, st);
+}
+
 int log2_exact(int x) {
   int k = 0;
   while ((1 << k) < x) ++k;
@@ -266,6 +287,66 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pages, const void* v_
   prm.num_blocks = s->num_blocks;
   return dispatch_mfma_dtype<true>(s->kv_dtype, s->d, prm.G, s->out_dtype, lo.workgroups, prm,
                                    (hipStream_t)stream);
+}
+
+gqa_status_t gqa_append_kv(const void* k_new, const void* v_new, int32_t new_dtype, void* k_cache,
+                           void* v_cache, const gqa_shape_t* s, const int32_t* positions,
+                           int32_t* skipped_count, void* stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !positions || !s) return GQA_ERR_INVALID_ARG;
+  if (new_dtype != GQA_F32 && new_dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(positions, 4) || !aligned(skipped_count, 4))
+    return GQA_ERR_INVALID_ARG;
+  const gqa_status_t st = gqa_shape_check(s);
+  if (st != GQA_OK) return st;
+  if (!(s->k_descale > 0.f) || !(s->v_descale > 0.f)) return GQA_ERR_INVALID_ARG;
+  gqa::AppendParams ap;
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.k_cache = k_cache;
+  ap.v_cache = v_cache;
+  ap.positions = positions;
+  ap.skipped = skipped_count;
+  ap.B = s->B;
+  ap.Hkv = s->Hkv;
+  ap.L = s->L;
+  ap.k_descale = s->k_descale;
+  ap.v_descale = s->v_descale;
+  ap.block_table = nullptr;
+  ap.block_shift = 0;
+  ap.max_blocks = 0;
+  ap.num_blocks = 0;
+  return launch_append<false>(new_dtype, s->kv_dtype, s->d, s->B, ap, (hipStream_t)stream);
+}
+
+gqa_status_t gqa_append_kv_paged(const void* k_new, const void* v_new, int32_t new_dtype, void* k_pages,
+                                 void* v_pages, const int32_t* block_table, const gqa_paged_shape_t* s,
+                                 const int32_t* positions, int32_t* skipped_count, void* stream) {
+  if (!k_new || !v_new || !k_pages || !v_pages || !block_table || !positions || !s) return GQA_ERR_INVALID_ARG;
+  if (new_dtype != GQA_F32 && new_dtype != GQA_BF16) return GQA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) ||
+      !aligned(positions, 4) || !aligned(skipped_count, 4) || !aligned(block_table, 4))
+    return GQA_ERR_INVALID_ARG;
+  const gqa_status_t st = gqa_paged_shape_check(s);
+  if (st != GQA_OK) return st;
+  if (!(s->k_descale > 0.f) || !(s->v_descale > 0.f)) return GQA_ERR_INVALID_ARG;
+  gqa::AppendParams ap;
+  ap.k_new = k_new;
+  ap.v_new = v_new;
+  ap.k_cache = k_pages;
+  ap.v_cache = v_pages;
+  ap.positions = positions;
+  ap.skipped = skipped_count;
+  ap.B = s->B;
+  ap.Hkv = s->Hkv;
+  ap.L = s->max_blocks * s->block_size;
+  ap.k_descale = s->k_descale;
+  ap.v_descale = s->v_descale;
+  ap.block_table = block_table;
+  ap.block_shift = log2_exact(s->block_size);
+  ap.max_blocks = s->max_blocks;
+  ap.num_blocks = s->num_blocks;
+  return launch_append<true>(new_dtype, s->kv_dtype, s->d, s->B, ap, (hipStream_t)stream);
 }
 
 uint64_t gqa_kv_bytes_per_token(uint32_t layers, uint32_t kv_heads, uint32_t head_dim,

@@ -139,6 +139,28 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pages, const void* v_
                               const gqa_paged_shape_t* shape, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* ------------------------------------------------------------------------------------------------
+ * Cache append: stores the new token's K and V rows before the decode that attends to them.  Row
+ * (b, j) of k_new / v_new ([B, Hkv, d], new_dtype GQA_F32 or GQA_BF16, 16-byte aligned) goes to
+ * position positions[b] (int32 [B], device) of sequence b, KV head j, converted to the cache's
+ * format: f32 as is; bf16 rounded to nearest even (overflow to infinity, NaN to 0x7FC0 with its
+ * sign); fp8-e4m3 as the code of x / descale (k_descale for K, v_descale for V, binary32 division)
+ * rounded to nearest even and saturated at +-448, NaN to 0x7F with its sign ("Grouped-Query
+ * Attention: How Sharing KV Heads Shrinks Inference Memory", section "FP8 KV cache: the other
+ * factor of two": real value = stored * descale).  A negative position skips the sequence.  A
+ * position >= L (dense) or >= max_blocks * block_size, or whose page-table entry lies outside
+ * [0, num_blocks) (paged), writes nothing for that sequence and adds one to *skipped_count (device
+ * int32, may be NULL).  Nothing else in the cache is touched.  Descales must be positive and finite.
+ * Enqueued on `stream`; asynchronous.  The shapes describe the cache as for the decode entry points
+ * (their q_dtype and out_dtype must still form a supported combination).
+ */
+gqa_status_t gqa_append_kv(const void* k_new, const void* v_new, int32_t new_dtype, void* k_cache,
+                           void* v_cache, const gqa_shape_t* shape, const int32_t* positions,
+                           int32_t* skipped_count, void* stream);
+gqa_status_t gqa_append_kv_paged(const void* k_new, const void* v_new, int32_t new_dtype, void* k_pages,
+                                 void* v_pages, const int32_t* block_table, const gqa_paged_shape_t* shape,
+                                 const int32_t* positions, int32_t* skipped_count, void* stream);
+
 /* KV-cache bytes per token: 2 (one K and one V tensor) * layers * kv_heads * head_dim * dtype_bytes
  * ("Grouped Query Attention: Why 8 KV Heads Decide Your Batch Size", section "Why does GQA decide
  * your batch size?").  Computed in 64-bit; host only. */

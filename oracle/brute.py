@@ -100,3 +100,47 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, q_dtype="f32
         kd.append(kb)
         vd.append(vb)
     return decode(q, kd, vd, seq_lens, scale, q_dtype, kv_dtype, k_descale, v_descale)
+
+
+def _to_f32(v):
+    """Round a Python float to binary32 (nearest even), overflowing to infinity."""
+    if math.isnan(v) or math.isinf(v):
+        return v
+    try:
+        return struct.unpack("<f", struct.pack("<f", v))[0]
+    except OverflowError:  # beyond the binary32 range after rounding
+        return math.copysign(math.inf, v)
+
+
+def encode_fp8_e4m3(x, descale=1.0):
+    """e4m3fn code of x / descale, both taken as binary32 and divided in binary32: exponent by
+    math.frexp, three mantissa bits rounded half to even by round(); saturates at +-448; NaN -> 0x7F
+    with the sign bit.  (An independent route to the oracle's nearest-code search.)"""
+    x32, s32 = _to_f32(x), _to_f32(descale)
+    if math.isnan(x32):
+        return 0x7F | (0x80 if math.copysign(1.0, x32) < 0 else 0)
+    # the double quotient rounded to binary32 is the correctly rounded binary32 quotient (53 >= 2*24+2)
+    y = _to_f32(x32 / s32) if s32 != 0 else _to_f32(math.copysign(math.inf, x32) if x32 else math.nan)
+    neg = math.copysign(1.0, y) < 0
+    sign = 0x80 if neg else 0
+    if math.isnan(y):
+        return 0x7F | sign
+    a = abs(y)
+    if a >= 448.0:
+        return 0x7E | sign
+    if a < 2.0 ** -6:
+        return sign | round(a * 512.0)            # subnormal multiples of 2^-9 (8 -> smallest normal)
+    m, e = math.frexp(a)                          # a = m * 2^e, m in [0.5, 1)
+    e -= 1                                        # a = (2m) * 2^e, 2m in [1, 2)
+    frac = round((2.0 * m - 1.0) * 8.0)
+    if frac == 8:
+        frac, e = 0, e + 1
+    return sign | ((e + 7) << 3) | frac
+
+
+def encode_bf16(x):
+    """bf16 bits of binary32 x, rounded to nearest even by integer arithmetic on its bits."""
+    u = struct.unpack("<I", struct.pack("<f", float(x)))[0]
+    if (u & 0x7FFFFFFF) > 0x7F800000:
+        return 0x7FC0 | ((u >> 16) & 0x8000)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF

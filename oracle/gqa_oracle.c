@@ -31,6 +31,10 @@
  *     position t sits at row t % block_size of it.  Pages are laid out [num_blocks][Hkv][block_size][d].
  *     The attention itself is the dense one over the un-paged cache.
  *
+ *   - Appending the new token's K and V rows to the cache, converted to the cache's storage format; an
+ *     fp8 cache stores the code of the value divided by the per-tensor descale ("Grouped-Query Attention:
+ *     How Sharing KV Heads Shrinks Inference Memory", section "FP8 KV cache: the other factor of two").
+ *
  * Readings where the pages are silent: seq_len 0 yields an all-zero output row; seq_len outside [0, L]
  * is an error (return code 2); a page-table entry of a live page outside [0, num_blocks) is an error
  * (return code 3) while entries of pages past a sequence's length are never read; the output is
@@ -253,4 +257,125 @@ int gqa_oracle_decode_paged(const void* q, int q_dtype, const void* k_pages, con
     head_output(&p, b, h, w_scratch, out + (size_t)r * d);
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Encoders (storage format of a value), written from the format definitions.
+ *
+ * bf16: the bf16 value nearest to the binary32 input, ties to the even bit pattern (round to nearest
+ *       even, overflowing to infinity as binary formats do); infinities stay; NaN becomes the quiet
+ *       NaN 0x7FC0 with the input's sign.
+ * fp8 e4m3fn: the input is first divided by the descale in binary32 (correctly rounded, as C does
+ *       it), then mapped to the finite e4m3fn value nearest to the quotient, found by trying every
+ *       code; ties go to the code with an even mantissa, and between +0 and -0 to the quotient's sign.
+ *       Values beyond the largest finite value 448 (infinities included) therefore saturate to +-448.
+ *       A NaN input becomes 0x7F with the input's sign bit. */
+uint16_t gqa_oracle_encode_bf16(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  if (isnan(x)) return (uint16_t)(0x7FC0u | sign);
+  if (isinf(x)) return (uint16_t)(sign | 0x7F80u);
+  /* candidates: the two bf16 patterns around x (truncation and the next one up in magnitude) */
+  const uint16_t lo = (uint16_t)(u >> 16);
+  const uint16_t hi = (uint16_t)(lo + 1);
+  const double dx = (double)x;
+  const double dlo = gqa_oracle_bf16_to_double(lo);
+  /* past the largest finite value the next pattern is infinity, which rounding treats as 2^128
+   * (the exponent range taken as unbounded), so large enough inputs round to infinity */
+  const double dhi = ((hi & 0x7FFFu) == 0x7F80u) ? copysign(ldexp(1.0, 128), dx) : gqa_oracle_bf16_to_double(hi);
+  const double elo = fabs(dx - dlo), ehi = fabs(dx - dhi);
+  if (elo < ehi) return lo;
+  if (ehi < elo) return hi;
+  return (lo & 1u) ? hi : lo; /* tie: even pattern */
+}
+
+uint8_t gqa_oracle_encode_fp8_e4m3(float x, float descale) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  if (isnan(x)) return (uint8_t)(0x7Fu | ((u >> 31) ? 0x80u : 0u));
+  const float y = x / descale; /* binary32, correctly rounded */
+  memcpy(&u, &y, 4);
+  const int neg = (int)(u >> 31);
+  /* at or past the largest finite value 448 the nearest finite value is +-448 (checked here so that
+   * the distances below stay exact: they are, for |y| < 448, in double) */
+  if (fabs((double)y) >= 448.0) return (uint8_t)(neg ? 0xFEu : 0x7Eu);
+  int best = -1;
+  double best_err = 0.0;
+  for (int c = 0; c < 256; ++c) {
+    const double v = gqa_oracle_fp8_e4m3_to_double((uint8_t)c);
+    if (isnan(v)) continue;
+    const double err = fabs((double)y - v);
+    if (best < 0 || err < best_err) {
+      best = c;
+      best_err = err;
+    } else if (err == best_err) {
+      const double vb = gqa_oracle_fp8_e4m3_to_double((uint8_t)best);
+      if (v == vb) { /* +0 and -0: keep the quotient's sign */
+        if (((c >> 7) & 1) == neg) best = c;
+      } else if ((best & 1) && !(c & 1)) { /* a true tie between neighbours: even mantissa */
+        best = c;
+      }
+    }
+  }
+  return (uint8_t)best;
+}
+
+/* Appends one row per (sequence, KV head): row (b, j) of k_new / v_new ([B][Hkv][d], new_dtype f32 or
+ * bf16) is stored, in the cache's format, at position positions[b] of sequence b's cache (dense
+ * [B][Hkv][L][d] when block_table is NULL, else pages [num_blocks][Hkv][block_size][d]).  A negative
+ * position skips the sequence; a position >= L, or one whose page-table entry lies outside
+ * [0, num_blocks), is not written and is counted.  Returns the count of such sequences, or -1 for bad
+ * arguments.  Nothing else in the cache changes. */
+int gqa_oracle_append(const void* k_new, const void* v_new, int new_dtype, void* k_cache, void* v_cache,
+                      int kv_dtype, double k_descale, double v_descale, const int32_t* positions, int B,
+                      int Hkv, int L, int d, const int32_t* block_table, int block_size, int max_blocks,
+                      int num_blocks) {
+  if (B < 0 || Hkv <= 0 || d <= 0 || L < 0) return -1;
+  if (new_dtype != ORACLE_F32 && new_dtype != ORACLE_BF16) return -1;
+  if (!elem_size(kv_dtype)) return -1;
+  if (block_table && (block_size <= 0 || max_blocks < 0 || num_blocks < 0)) return -1;
+  const int esz = elem_size(kv_dtype);
+  int skipped = 0;
+  for (int b = 0; b < B; ++b) {
+    const int t = positions[b];
+    if (t < 0) continue;
+    if (t >= L) {
+      ++skipped;
+      continue;
+    }
+    size_t page = 0;
+    if (block_table) {
+      const int32_t pg = block_table[(size_t)b * max_blocks + t / block_size];
+      if (pg < 0 || pg >= num_blocks) {
+        ++skipped;
+        continue;
+      }
+      page = (size_t)pg;
+    }
+    for (int j = 0; j < Hkv; ++j) {
+      const size_t row = block_table
+          ? ((page * Hkv + j) * (size_t)block_size + (size_t)(t % block_size)) * d
+          : (((size_t)b * Hkv + j) * (size_t)L + (size_t)t) * d;
+      for (int c = 0; c < d; ++c) {
+        const size_t src = ((size_t)b * Hkv + j) * d + c;
+        for (int kv = 0; kv < 2; ++kv) {
+          const void* in = kv ? v_new : k_new;
+          void* cache = kv ? v_cache : k_cache;
+          const double descale = kv ? v_descale : k_descale;
+          const float x = (float)load_elem(in, new_dtype, src); /* exact: f32 or bf16 input */
+          char* dst = (char*)cache + (row + c) * esz;
+          if (kv_dtype == ORACLE_F32) {
+            memcpy(dst, &x, 4);
+          } else if (kv_dtype == ORACLE_BF16) {
+            const uint16_t h = gqa_oracle_encode_bf16(x);
+            memcpy(dst, &h, 2);
+          } else {
+            *(uint8_t*)dst = gqa_oracle_encode_fp8_e4m3(x, (float)descale);
+          }
+        }
+      }
+    }
+  }
+  return skipped;
 }

@@ -36,6 +36,13 @@ def lib():
                                               c_void, c_dbl, c_int, c_int, c_int, c_int, c_int, c_int,
                                               c_int, c_void, c_int, c_void, c_void]
         L.gqa_oracle_decode_paged.restype = c_int
+        L.gqa_oracle_encode_bf16.argtypes = [ctypes.c_float]
+        L.gqa_oracle_encode_bf16.restype = ctypes.c_uint16
+        L.gqa_oracle_encode_fp8_e4m3.argtypes = [ctypes.c_float, ctypes.c_float]
+        L.gqa_oracle_encode_fp8_e4m3.restype = ctypes.c_uint8
+        L.gqa_oracle_append.argtypes = [c_void, c_void, c_int, c_void, c_void, c_int, c_dbl, c_dbl, c_void,
+                                        c_int, c_int, c_int, c_int, c_void, c_int, c_int, c_int]
+        L.gqa_oracle_append.restype = c_int
         L.gqa_oracle_kv_bytes_per_token.argtypes = [ctypes.c_uint64] * 4
         L.gqa_oracle_kv_bytes_per_token.restype = ctypes.c_uint64
         L.gqa_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -173,3 +180,40 @@ def bf16_to_double(bits):
 
 def fp8_e4m3_to_double(code):
     return lib().gqa_oracle_fp8_e4m3_to_double(int(code))
+
+
+def encode_bf16(x):
+    """bf16 bit pattern of the binary32 value x (round to nearest even)."""
+    return int(lib().gqa_oracle_encode_bf16(float(np.float32(x))))
+
+
+def encode_fp8_e4m3(x, descale=1.0):
+    """e4m3fn code of binary32 x / descale (nearest finite value, ties to even, saturating)."""
+    return int(lib().gqa_oracle_encode_fp8_e4m3(float(np.float32(x)), float(np.float32(descale))))
+
+
+def append(k_new, v_new, new_dtype, k_cache, v_cache, kv_dtype, positions, k_descale=1.0, v_descale=1.0,
+           block_table=None):
+    """Writes the new rows into numpy copies of the caches; returns (k_cache, v_cache, skipped).
+
+    k_new, v_new: [B, Hkv, d] in new_dtype ("f32" or "bf16"); caches dense [B, Hkv, L, d] or, with a
+    block_table [B, max_blocks], pages [num_blocks, Hkv, block_size, d]."""
+    kn, vn = raw(k_new, new_dtype), raw(v_new, new_dtype)
+    kc, vc = raw(k_cache, kv_dtype).copy(), raw(v_cache, kv_dtype).copy()
+    B, Hkv, d = kn.shape
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32).reshape(-1))
+    if pos.shape[0] != B or vn.shape != kn.shape or vc.shape != kc.shape:
+        raise ValueError("shape mismatch")
+    if block_table is None:
+        L, bt, bs, mb, nb = kc.shape[2], None, 0, 0, 0
+    else:
+        bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+        nb, bs, mb = kc.shape[0], kc.shape[2], bt.shape[1]
+        L = bs * mb
+    rc = lib().gqa_oracle_append(kn.ctypes.data, vn.ctypes.data, DTYPES[new_dtype], kc.ctypes.data,
+                                 vc.ctypes.data, DTYPES[kv_dtype], float(k_descale), float(v_descale),
+                                 pos.ctypes.data, B, Hkv, L, d, None if bt is None else bt.ctypes.data,
+                                 bs, mb, nb)
+    if rc < 0:
+        raise ValueError("oracle: bad append arguments")
+    return kc, vc, rc
