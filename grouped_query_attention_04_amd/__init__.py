@@ -40,6 +40,11 @@ class Shape(ctypes.Structure):
                 ("num_workgroups", ctypes.c_int32)]
 
 
+class TpRank(ctypes.Structure):
+    _fields_ = [("q_head_begin", ctypes.c_int32), ("q_head_end", ctypes.c_int32),
+                ("kv_head_begin", ctypes.c_int32), ("kv_head_end", ctypes.c_int32)]
+
+
 class PagedShape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
@@ -51,7 +56,8 @@ class PagedShape(ctypes.Structure):
 
 EXPORTS = ["gqa_shape_check", "gqa_decode_workspace_bytes", "gqa_workspace_init", "gqa_decode",
            "gqa_paged_shape_check", "gqa_decode_paged_workspace_bytes", "gqa_paged_workspace_init",
-           "gqa_decode_paged", "gqa_append_kv", "gqa_append_kv_paged", "gqa_kv_bytes_per_token", "gqa_validate_seq_lens", "gqa_stream_read",
+           "gqa_decode_paged", "gqa_append_kv", "gqa_append_kv_paged", "gqa_tp_plan",
+           "gqa_max_concurrency", "gqa_max_cached_tokens", "gqa_kv_bytes_per_token", "gqa_validate_seq_lens", "gqa_stream_read",
            "gqa_stream_read_sink_words", "gqa_status_string"]
 
 
@@ -82,6 +88,13 @@ def _load():
     lib.gqa_append_kv.restype = ctypes.c_int
     lib.gqa_append_kv_paged.argtypes = [vp, vp, i32, vp, vp, vp, pP, vp, vp, vp]
     lib.gqa_append_kv_paged.restype = ctypes.c_int
+    u64 = ctypes.c_uint64
+    lib.gqa_tp_plan.argtypes = [i32, i32, i32, ctypes.POINTER(TpRank), ctypes.POINTER(i32)]
+    lib.gqa_tp_plan.restype = ctypes.c_int
+    lib.gqa_max_concurrency.argtypes = [u64, u64, u64]
+    lib.gqa_max_concurrency.restype = u64
+    lib.gqa_max_cached_tokens.argtypes = [u64, u64]
+    lib.gqa_max_cached_tokens.restype = u64
     lib.gqa_kv_bytes_per_token.argtypes = [ctypes.c_uint32] * 4
     lib.gqa_kv_bytes_per_token.restype = ctypes.c_uint64
     lib.gqa_validate_seq_lens.argtypes = [vp, i32, i32, vp, vp]
@@ -133,6 +146,22 @@ def workspace_bytes(shape) -> int:
 
 def kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes=2) -> int:
     return int(lib.gqa_kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes))
+
+
+def tp_plan(num_q_heads, num_kv_heads, tp_size):
+    """Per-rank (q_begin, q_end, kv_begin, kv_end) and the KV heads held over all ranks."""
+    ranks = (TpRank * max(int(tp_size), 1))()
+    held = ctypes.c_int32(0)
+    _check(lib.gqa_tp_plan(int(num_q_heads), int(num_kv_heads), int(tp_size), ranks, ctypes.byref(held)))
+    return [(r.q_head_begin, r.q_head_end, r.kv_head_begin, r.kv_head_end) for r in ranks[:tp_size]], held.value
+
+
+def max_concurrency(free_bytes, bytes_per_token, context_tokens) -> int:
+    return int(lib.gqa_max_concurrency(int(free_bytes), int(bytes_per_token), int(context_tokens)))
+
+
+def max_cached_tokens(free_bytes, bytes_per_token) -> int:
+    return int(lib.gqa_max_cached_tokens(int(free_bytes), int(bytes_per_token)))
 
 
 def _stream_handle(device):

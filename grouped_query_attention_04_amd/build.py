@@ -5,7 +5,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "gqa_api.hip")
+SRCS = [os.path.join(PKG, "csrc", "gqa_api.hip"), os.path.join(PKG, "csrc", "gqa_plan.cpp")]
 LIB = os.path.join(PKG, "libgqa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -20,7 +20,7 @@ FLAGS = [
 def build(verbose: bool = False) -> str:
     """Always recompiles; returns the library path."""
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           SRC, "-o", LIB + ".tmp"]
+           *SRCS, "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -167,6 +167,35 @@ gqa_status_t gqa_append_kv_paged(const void* k_new, const void* v_new, int32_t n
 uint64_t gqa_kv_bytes_per_token(uint32_t layers, uint32_t kv_heads, uint32_t head_dim,
                                 uint32_t dtype_bytes);
 
+/* ------------------------------------------------------------------------------------------------
+ * Serving planners (host only, no HIP call).
+ *
+ * Tensor-parallel head sharding ("Grouped Query Attention: Why 8 KV Heads Decide Your Batch Size",
+ * section "What breaks when num_kv_heads is smaller than your tensor-parallel degree?";
+ * "Grouped-Query Attention: How Sharing KV Heads Shrinks Inference Memory", section "Why not always go
+ * to one KV head?"): rank r of tp_size takes query heads [r * Hq / tp, (r + 1) * Hq / tp) and holds
+ * every KV head they read (h -> h / G, G = Hq / Hkv).  When tp_size exceeds Hkv, or neither divides
+ * the other, a KV head is held by several ranks: *kv_heads_held (summed over ranks) then exceeds Hkv,
+ * and the ratio is the replication factor.  Requires Hq % Hkv == 0 and Hq % tp_size == 0, else
+ * GQA_ERR_INVALID_ARG.  ranks (tp_size entries) and kv_heads_held may each be NULL.
+ * A rank's KV bytes per token: gqa_kv_bytes_per_token(layers, kv_head_end - kv_head_begin, ...).
+ */
+typedef struct {
+  int32_t q_head_begin, q_head_end;   /* query heads [begin, end) */
+  int32_t kv_head_begin, kv_head_end; /* KV heads [begin, end) held by the rank */
+} gqa_tp_rank_t;
+
+gqa_status_t gqa_tp_plan(int32_t num_q_heads, int32_t num_kv_heads, int32_t tp_size, gqa_tp_rank_t* ranks,
+                         int32_t* kv_heads_held);
+
+/* Sequences of context_tokens that fit in free_bytes of cache: free / (bytes_per_token * context),
+ * rounded down, 0 when either factor is 0 ("Grouped Query Attention: Why 8 KV Heads Decide Your Batch
+ * Size", section "Why does GQA decide your batch size?").  Exact for all 64-bit inputs. */
+uint64_t gqa_max_concurrency(uint64_t free_bytes, uint64_t bytes_per_token, uint64_t context_tokens);
+
+/* Cached tokens that fit in free_bytes: free / bytes_per_token rounded down (0 if bytes_per_token is 0). */
+uint64_t gqa_max_cached_tokens(uint64_t free_bytes, uint64_t bytes_per_token);
+
 /* Test helper: writes the number of seq_lens entries outside [0, L] to *bad_count (device memory).
  * Enqueued on `stream`; does not synchronise.  Returns GQA_ERR_INVALID_ARG for null or misaligned
  * pointers or B <= 0. */
