@@ -144,3 +144,25 @@ def encode_bf16(x):
     if (u & 0x7FFFFFFF) > 0x7F800000:
         return 0x7FC0 | ((u >> 16) & 0x8000)
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+
+
+def prefill(q, k, v, scale, dtype="f32", causal=True):
+    """q nested [B][Hq][S][d], k, v nested [B][Hkv][S][d] (raw storage); position i of head h attends
+    to positions t <= i (all t when not causal) of KV head h // G.  Builds each row's decode problem
+    over the first i + 1 positions and hands it to ``decode``."""
+    B = len(q)
+    Hq, S = len(q[0]), len(q[0][0])
+    Hkv = len(k[0])
+    out = []
+    for b in range(B):
+        heads = []
+        for h in range(Hq):
+            rows = []
+            for i in range(S):
+                n = i + 1 if causal else S
+                # a one-sequence decode with Hkv query slots (group size 1): slot j reads KV head j
+                res = decode([[q[b][h][i]] * Hkv], [k[b]], [v[b]], [n], scale, dtype, dtype)
+                rows.append(res[0][h // (Hq // Hkv)])
+            heads.append(rows)
+        out.append(heads)
+    return out

@@ -35,6 +35,11 @@
  *     fp8 cache stores the code of the value divided by the per-tensor descale ("Grouped-Query Attention:
  *     How Sharing KV Heads Shrinks Inference Memory", section "FP8 KV cache: the other factor of two").
  *
+ *   - Causal prefill over a prompt of S tokens ("Grouped Query Attention: Why 8 KV Heads Decide Your
+ *     Batch Size", section "Why doesn't GQA speed up my fine-tuned model?", the scaled_dot_product_attention
+ *     call with is_causal and enable_gqa): q [B][Hq][S][d], k and v [B][Hkv][S][d]; query position i
+ *     of head h attends to key positions t <= i of KV head floor(h / G) (without the mask: all S).
+ *
  * Readings where the pages are silent: seq_len 0 yields an all-zero output row; seq_len outside [0, L]
  * is an error (return code 2); a page-table entry of a live page outside [0, num_blocks) is an error
  * (return code 3) while entries of pages past a sequence's length are never read; the output is
@@ -378,4 +383,54 @@ int gqa_oracle_append(const void* k_new, const void* v_new, int new_dtype, void*
     }
   }
   return skipped;
+}
+
+/* ------------------------------------------------------------------------------------------------
+ * Prefill: out[b][h][i][:] = sum over t < n_i of softmax_t(scale * q[b][h][i] . k[b][j][t]) v[b][j][t],
+ * j = floor(h / G), n_i = i + 1 when causal, else S.  rows == NULL: every (b, h, i) into out
+ * [B][Hq][S][d]; otherwise the nrows listed triples (b, h, i) into out [nrows][d].  w_scratch holds S
+ * doubles.  Returns 0 or 1 (bad arguments). */
+int gqa_oracle_prefill(const void* q, const void* k, const void* v, int dtype, double scale, int causal,
+                       int B, int Hq, int Hkv, int S, int d, const int32_t* rows, int nrows,
+                       double* w_scratch, double* out) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || S < 0 || d <= 0 || Hq % Hkv != 0 || !elem_size(dtype)) return 1;
+  const int G = Hq / Hkv;
+  const long long total = rows ? nrows : (long long)B * Hq * S;
+  for (long long r = 0; r < total; ++r) {
+    int b, h, i;
+    if (rows) {
+      b = rows[3 * r];
+      h = rows[3 * r + 1];
+      i = rows[3 * r + 2];
+      if (b < 0 || b >= B || h < 0 || h >= Hq || i < 0 || i >= S) return 1;
+    } else {
+      b = (int)(r / ((long long)Hq * S));
+      h = (int)((r / S) % Hq);
+      i = (int)(r % S);
+    }
+    const int j = h / G;
+    const int n = causal ? i + 1 : S;
+    const size_t qrow = (((size_t)b * Hq + h) * (size_t)S + (size_t)i) * d;
+    const size_t kvbase = ((size_t)b * Hkv + j) * (size_t)S * d;
+    double m = -INFINITY;
+    for (int t = 0; t < n; ++t) {
+      double dot = 0.0;
+      for (int c = 0; c < d; ++c)
+        dot += load_elem(q, dtype, qrow + c) * load_elem(k, dtype, kvbase + (size_t)t * d + c);
+      w_scratch[t] = dot * scale;
+      if (w_scratch[t] > m) m = w_scratch[t];
+    }
+    double z = 0.0;
+    for (int t = 0; t < n; ++t) {
+      w_scratch[t] = exp(w_scratch[t] - m);
+      z += w_scratch[t];
+    }
+    double* o = out + (size_t)r * d;
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int t = 0; t < n; ++t) acc += (w_scratch[t] / z) * load_elem(v, dtype, kvbase + (size_t)t * d + c);
+      o[c] = acc;
+    }
+  }
+  return 0;
 }

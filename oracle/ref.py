@@ -43,6 +43,9 @@ def lib():
         L.gqa_oracle_append.argtypes = [c_void, c_void, c_int, c_void, c_void, c_int, c_dbl, c_dbl, c_void,
                                         c_int, c_int, c_int, c_int, c_void, c_int, c_int, c_int]
         L.gqa_oracle_append.restype = c_int
+        L.gqa_oracle_prefill.argtypes = [c_void, c_void, c_void, c_int, c_dbl, c_int, c_int, c_int, c_int,
+                                         c_int, c_int, c_void, c_int, c_void, c_void]
+        L.gqa_oracle_prefill.restype = c_int
         L.gqa_oracle_kv_bytes_per_token.argtypes = [ctypes.c_uint64] * 4
         L.gqa_oracle_kv_bytes_per_token.restype = ctypes.c_uint64
         L.gqa_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -217,3 +220,27 @@ def append(k_new, v_new, new_dtype, k_cache, v_cache, kv_dtype, positions, k_des
     if rc < 0:
         raise ValueError("oracle: bad append arguments")
     return kc, vc, rc
+
+
+def prefill(q, k, v, scale, dtype="bf16", causal=True, rows=None):
+    """Prefill attention: q [B,Hq,S,d], k, v [B,Hkv,S,d] (raw storage of dtype).  Returns out
+    [B,Hq,S,d] (rows None) or [len(rows), d] for the listed (b, h, i) triples, float64."""
+    qa, ka, va = raw(q, dtype), raw(k, dtype), raw(v, dtype)
+    if qa.ndim != 4 or ka.ndim != 4 or va.shape != ka.shape:
+        raise ValueError("q must be [B,Hq,S,d]; k and v [B,Hkv,S,d]")
+    B, Hq, S, d = qa.shape
+    Bk, Hkv, Sk, dk = ka.shape
+    if (Bk, Sk, dk) != (B, S, d):
+        raise ValueError("q and k/v disagree on B, S or d")
+    if rows is None:
+        r, nrows, out = None, 0, np.zeros((B, Hq, S, d), dtype=np.float64)
+    else:
+        r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
+        nrows, out = r.shape[0], np.zeros((r.shape[0], d), dtype=np.float64)
+    w = np.zeros(max(S, 1), dtype=np.float64)
+    rc = lib().gqa_oracle_prefill(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, DTYPES[dtype], float(scale),
+                                  1 if causal else 0, B, Hq, Hkv, S, d, None if r is None else r.ctypes.data,
+                                  nrows, w.ctypes.data, out.ctypes.data)
+    _raise(rc)
+    del qa, ka, va
+    return out
