@@ -11,6 +11,9 @@ permutation (gqa_decode_paged); the KV bytes counted are the same.  With --appen
 the new token's K and V rows (bf16, converted to the cache format: fp8 caches quantise) at position
 seq_lens[b] - 1 of every sequence, then decodes; the KV bytes counted are the same.
 
+With --prefill NAME (prefill-8b, prefill-70b) it instead times causal GQA prefill (gqa_prefill) and
+reports matmul TFLOP/s against the bf16 matrix-core peak.
+
 Prints one JSON line on stdout (diagnostics go to stderr).
 """
 import argparse
@@ -27,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV GB/s and % HBM roofline for GQA decode (Hq=64,Hkv=8,d=128,bf16)"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of an MI355X
 # rocprofv3 counter summaries of the 70B-shaped layer, keyed by page size (0 = dense cache)
 TRAFFIC_SUMMARY = {0: os.path.join(ROOT, "profiles", "gqa_decode_llama70b_traffic.md"),
                    16: os.path.join(ROOT, "profiles", "gqa_decode_paged16_llama70b_traffic.md")}
@@ -83,6 +87,88 @@ def cpu_baseline(case, groups_b, paged=None):
                       f"{kv_bytes / 1e6:.1f} MB of KV), single-threaded C, {dt:.1f} s"}
 
 
+def prefill_cpu_baseline(case, nrows=4000):
+    """Time the fp64 oracle (single thread) on a sample of causal prefill rows, as TFLOP/s."""
+    from oracle import ref
+
+    import numpy as np
+
+    w = case["workload"]
+    random_rows = []
+    gen = np.random.default_rng(7)
+    for _ in range(nrows):
+        random_rows.append((int(gen.integers(w.B)), int(gen.integers(w.Hq)), int(gen.integers(w.S))))
+    flops = sum(4 * w.d * (i + 1) for _, _, i in random_rows)
+    t0 = time.perf_counter()
+    ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", True, rows=random_rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 8), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nrows} random (batch, head, position) rows of the same prompt, "
+                      f"{flops / 1e9:.2f} GFLOP, single-threaded C, {dt:.1f} s"}
+
+
+def bench_prefill(args):
+    import torch
+
+    import grouped_query_attention_04_amd as gqa
+    import workloads
+
+    w = workloads.PREFILL_WORKLOADS[args.prefill]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"prefill {args.prefill}: {w.name}; generating inputs")
+    case = workloads.make_prefill(args.prefill)
+    q, k, v = (case[n].to(dev) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    shape = gqa.PrefillShape(w.B, w.Hq, w.Hkv, w.S, w.d, gqa.BF16, gqa.BF16, 1)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    shape_ref = ctypes.byref(shape)
+    scale = float(case["scale"])
+
+    def step():
+        rc = gqa.lib.gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), scale, out.data_ptr(), shape_ref, sh)
+        if rc:
+            raise RuntimeError(gqa.status_string(rc))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_ms = sum(launch_ms) / len(launch_ms)
+    achieved = w.flops / (avg_ms * 1e-3) / 1e12
+    log(f"step {ms_per_step * 1e3:.1f} us wall ({value:.1f} TFLOP/s); kernel avg {avg_ms * 1e3:.1f} us "
+        f"(p10 {launch_ms[len(launch_ms) // 10] * 1e3:.1f}, p90 {launch_ms[9 * len(launch_ms) // 10] * 1e3:.1f}); "
+        f"{achieved:.1f} TFLOP/s = {100 * achieved / MFMA_BF16_PEAK_TFLOPS:.1f}% of the bf16 MFMA peak")
+    result = {
+        "metric": "causal GQA prefill TFLOP/s (bf16)", "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "S": w.S,
+                   "causal": True, "flops_per_step": w.flops, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample of the same prompt")
+        result["cpu_baseline"] = prefill_cpu_baseline(case)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,6 +177,8 @@ def main():
     ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4-mha, 4-gqa, 4-mqa, 5)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated (0 = enough for 2 GiB)")
     ap.add_argument("--workgroups", type=int, default=0, help="workgroups (0 = library choice)")
+    ap.add_argument("--prefill", default="", metavar="NAME",
+                    help="time causal prefill instead (prefill-8b or prefill-70b)")
     ap.add_argument("--append", action="store_true",
                     help="each step appends the new token's K/V rows before the decode")
     ap.add_argument("--paged", type=int, default=0, metavar="BS",
@@ -106,6 +194,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world})", file=sys.stderr)
         return 2
+
+    if args.prefill:
+        return bench_prefill(args)
 
     import torch
 

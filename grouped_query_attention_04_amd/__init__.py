@@ -40,6 +40,12 @@ class Shape(ctypes.Structure):
                 ("num_workgroups", ctypes.c_int32)]
 
 
+class PrefillShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("S", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("causal", ctypes.c_int32)]
+
+
 class TpRank(ctypes.Structure):
     _fields_ = [("q_head_begin", ctypes.c_int32), ("q_head_end", ctypes.c_int32),
                 ("kv_head_begin", ctypes.c_int32), ("kv_head_end", ctypes.c_int32)]
@@ -56,7 +62,8 @@ class PagedShape(ctypes.Structure):
 
 EXPORTS = ["gqa_shape_check", "gqa_decode_workspace_bytes", "gqa_workspace_init", "gqa_decode",
            "gqa_paged_shape_check", "gqa_decode_paged_workspace_bytes", "gqa_paged_workspace_init",
-           "gqa_decode_paged", "gqa_append_kv", "gqa_append_kv_paged", "gqa_tp_plan",
+           "gqa_decode_paged", "gqa_append_kv", "gqa_append_kv_paged", "gqa_prefill_shape_check",
+           "gqa_prefill", "gqa_tp_plan",
            "gqa_max_concurrency", "gqa_max_cached_tokens", "gqa_kv_bytes_per_token", "gqa_validate_seq_lens", "gqa_stream_read",
            "gqa_stream_read_sink_words", "gqa_status_string"]
 
@@ -88,6 +95,11 @@ def _load():
     lib.gqa_append_kv.restype = ctypes.c_int
     lib.gqa_append_kv_paged.argtypes = [vp, vp, i32, vp, vp, vp, pP, vp, vp, vp]
     lib.gqa_append_kv_paged.restype = ctypes.c_int
+    pF = ctypes.POINTER(PrefillShape)
+    lib.gqa_prefill_shape_check.argtypes = [pF]
+    lib.gqa_prefill_shape_check.restype = ctypes.c_int
+    lib.gqa_prefill.argtypes = [vp, vp, vp, ctypes.c_float, vp, pF, vp]
+    lib.gqa_prefill.restype = ctypes.c_int
     u64 = ctypes.c_uint64
     lib.gqa_tp_plan.argtypes = [i32, i32, i32, ctypes.POINTER(TpRank), ctypes.POINTER(i32)]
     lib.gqa_tp_plan.restype = ctypes.c_int
@@ -329,6 +341,39 @@ def append_kv_paged(k_new, v_new, k_pages, v_pages, block_table, positions, *, k
                                        k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
                                        ctypes.byref(shape), positions.data_ptr(),
                                        None if skipped is None else skipped.data_ptr(), _stream_handle(dev)))
+
+
+def prefill(q, k, v, scale=None, out=None, *, out_dtype=None, causal=True):
+    """GQA attention of a prompt over itself: q [B,Hq,S,d], k, v [B,Hkv,S,d] (bf16, contiguous, one
+    device).  Query position i of head h attends to positions <= i (all, if not causal) of KV head
+    h // (Hq // Hkv).  Returns out [B,Hq,S,d] (dtype out_dtype, default bf16).  scale defaults to
+    1/sqrt(d).  Enqueued on torch's current stream."""
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("expected q [B,Hq,S,d], k and v [B,Hkv,S,d]")
+    B, Hq, S, d = q.shape
+    if k.shape[0] != B or k.shape[2] != S or k.shape[3] != d:
+        raise ValueError("q and k/v disagree on B, S or d")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("prefill takes bfloat16 q, k and v")
+    tensors = [q, k, v] + ([out] if out is not None else [])
+    dev = q.device
+    if dev.type != "cuda" or any(t.device != dev for t in tensors):
+        raise ValueError("all tensors must live on one CUDA (HIP) device")
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous")
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    if out is None:
+        out = torch.empty((B, Hq, S, d), dtype=out_dtype, device=dev)
+    elif out.shape != (B, Hq, S, d) or out.dtype != out_dtype:
+        raise ValueError("out must be [B,Hq,S,d] of dtype out_dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    shape = PrefillShape(B, Hq, k.shape[1], S, d, BF16, _CODE[out_dtype], 1 if causal else 0)
+    with torch.cuda.device(dev):
+        _check(lib.gqa_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), float(scale), out.data_ptr(),
+                               ctypes.byref(shape), _stream_handle(dev)))
+    return out
 
 
 def validate_seq_lens(seq_lens, L) -> int:

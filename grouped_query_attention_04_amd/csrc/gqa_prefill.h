@@ -1,0 +1,235 @@
+// gqa_prefill.h -- HIP kernel (gfx950 / CDNA4) for grouped-query-attention prefill over a prompt.
+//
+// The arithmetic is the scaled_dot_product_attention call with is_causal and enable_gqa of "Grouped
+// Query Attention: Why 8 KV Heads Decide Your Batch Size" (section "Why doesn't GQA speed up my
+// fine-tuned model?"): query position i of head h attends to key positions t <= i of KV head
+// floor(h / G), softmax-weighted over the values.  Unlike decode this is a dense contraction, run on
+// the matrix cores.
+//
+// Work decomposition.  A workgroup owns one (batch b, KV head j, block of BM query positions) and all
+// G query heads of the group, so every K/V tile it stages in LDS serves G heads at once -- the
+// grouping is used, not expanded (same page, the repeat_kv discussion).  Its 256 rows (G heads x BM
+// positions, BM = 256 / G) are split over 4 waves of 64 rows (four 16-row tiles).  Keys are taken
+// in blocks of 32 through two LDS buffers: while the waves compute on one, the next block's loads
+// are in flight and land in the other.
+//
+// Per block and wave (lane l, quad q = l / 16, r = l % 16):
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16, two 16-key halves; A = K rows from LDS, B = the wave's
+//   query rows (registers).  Lane l holds S[row r][key 16h + 4q + i].
+//   O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with the 32 keys of the block as the contraction:
+//   k-slot 8q + e is key 4q + e (e < 4) or 16 + 4q + (e - 4) (e >= 4), so P^T's B operand is the
+//   lane's own eight probabilities, and A = V^T comes from two ds_read_b64_tr_b16 of the LDS V tile.
+//   Lane l holds O[row r][d = 16m + 4q + i]; the row's running max and sum live in the same lanes.
+#pragma once
+
+#include "gqa_kernels.h"
+
+namespace gqa {
+
+struct PrefillParams {
+  const void* q;  // [B][Hq][S][D] bf16
+  const void* k;  // [B][Hkv][S][D] bf16
+  const void* v;
+  void* out;      // [B][Hq][S][D] OutT
+  int B, Hq, Hkv, S, G;
+  int bm_shift;   // BM = 1 << bm_shift query positions per workgroup (BM * G = 256 rows)
+  int nqb;        // query blocks per (b, j)
+  float qk_scale; // scale * log2(e)
+};
+
+template <int D, typename OutT, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) prefill_mfma_kernel(PrefillParams p) {
+  constexpr int KB = 32;                // keys per block
+  constexpr int NT = 4;                 // 16-row tiles per wave
+  constexpr int KS = D / 32;            // k-steps of QK^T
+  constexpr int MT = D / 16;            // m-tiles of PV (head-dim columns)
+  constexpr int ROWB = D * 2;           // bytes per K/V row
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int TILEB = KB * ROWB;      // bytes of one K (or V) block
+  constexpr int NLD = TILEB / 16 / 256; // 16-byte loads per thread per block and tensor
+  __shared__ __attribute__((aligned(16))) char ks[2][TILEB];
+  __shared__ __attribute__((aligned(16))) char vs[2][TILEB];
+
+  // heaviest query blocks first: block index -> (query block, batch, KV head)
+  const int nbj = p.B * p.Hkv;
+  const int qb = p.nqb - 1 - (int)(blockIdx.x / nbj);
+  const int bj = (int)(blockIdx.x % nbj);
+  const int b = bj / p.Hkv, j = bj % p.Hkv;
+  const int BM = 1 << p.bm_shift;
+  const int w = uniform((int)threadIdx.x / 64);
+  const int l = threadIdx.x % 64;
+  const int q = l / 16;
+  const int r = l % 16;
+
+  // the wave's rows: row rho = 64 w + 16 nt + r is head g = rho / BM, position qb * BM + rho % BM
+  int pos[NT];
+  int head[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int rho = 64 * w + 16 * nt + r;
+    head[nt] = j * p.G + (rho >> p.bm_shift);
+    pos[nt] = qb * BM + (rho & (BM - 1));
+  }
+  // positions covered by the wave (for skipping blocks it cannot see) and by the workgroup
+  const int wave_lo = uniform(qb * BM + ((64 * w) & (BM - 1)));
+  const int wave_hi = uniform(min(p.S - 1, wave_lo + min(64, BM) - 1));
+  const int wg_hi = min(p.S, (qb + 1) * BM);  // exclusive
+  const int nkb = CAUSAL ? (wg_hi + KB - 1) / KB : (p.S + KB - 1) / KB;
+
+  // query rows in the B-operand layout of QK^T (zero for positions past the prompt)
+  bf16x8_t bq[NT][KS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (((size_t)b * p.Hq + head[nt]) * p.S + pos[nt]) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4_t v = {0, 0, 0, 0};
+      if (pos[nt] < p.S) v = *reinterpret_cast<const u32x4_t*>(qr + 32 * s + 8 * q);
+      bq[nt][s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // K/V blocks of this (b, j): buffer descriptors over the prompt (keys past S read as zero)
+  const size_t head_off = ((size_t)b * p.Hkv + j) * (size_t)p.S * ROWB;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(p.k) + head_off, (uint32_t)p.S * ROWB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(p.v) + head_off, (uint32_t)p.S * ROWB);
+  u32x4_t ldk[NLD], ldv[NLD];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const uint32_t off = (uint32_t)kb * TILEB + (threadIdx.x + 256 * u) * 16;
+      ldk[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      ldv[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+  };
+  // LDS placement: K chunk c of key row x at chunk c ^ (x % CPR); V as in the decode kernel's tile
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = threadIdx.x + 256 * u;
+      const int row = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<u32x4_t*>(ks[buf] + row * ROWB + ((ch ^ (row % CPR)) * 16)) = ldk[u];
+      *reinterpret_cast<u32x4_t*>(vs[buf] + row * ROWB + ((ch ^ (2 * (row % (D / 16)))) * 16)) = ldv[u];
+    }
+  };
+
+  float m_run[NT], l_run[NT];
+  f32x4_t o[NT][MT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](int kb, int buf) {
+    const char* kt_lds = ks[buf];
+    const uint32_t vt_lds = (uint32_t)(uintptr_t)(GQA_LDS char*)vs[buf];
+    // -- scores S^T for the two 16-key halves
+    f32x4_t sc[2][NT];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      bf16x8_t ak[KS];
+      const int row = 16 * hf + r;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int ch = 4 * s + q;
+        ak[s] = *reinterpret_cast<const bf16x8_t*>(kt_lds + row * ROWB + ((ch ^ (row % CPR)) * 16));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[s], bq[nt][s], acc, 0, 0, 0);
+        sc[hf][nt] = acc * p.qk_scale;
+      }
+    }
+    // -- masks: keys past the prompt, and (causal) keys after the row's position
+    const int k0 = kb * KB;
+    if ((CAUSAL && k0 + KB - 1 > wave_lo) || k0 + KB > p.S) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * hf + 4 * q + i;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            if (key >= p.S || (CAUSAL && key > pos[nt])) sc[hf][nt][i] = -INFINITY;
+        }
+    }
+    // -- online softmax; P^T in the B-operand layout of PV (k-slot 8q + e, see the header)
+    bf16x8_t bp[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        mx = fmaxf(mx, fmaxf(fmaxf(sc[hf][nt][0], sc[hf][nt][1]), fmaxf(sc[hf][nt][2], sc[hf][nt][3])));
+      mx = wave_max_xor_16_32(mx);
+      const float m_new = fmaxf(m_run[nt], mx);
+      // a row that has seen no key yet (m_new = -inf) keeps alpha = 1 and gets p = 0
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+      m_run[nt] = m_new;
+      uint32_t pk[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2) {
+          const uint32_t lo = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[hf][nt][2 * i2] - m_use));
+          const uint32_t hi = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[hf][nt][2 * i2 + 1] - m_use));
+          psum += bf16_bits_to_float(lo) + bf16_bits_to_float(hi);
+          pk[2 * hf + i2] = lo | (hi << 16);
+        }
+      l_run[nt] = l_run[nt] * alpha + psum;
+      bp[nt] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+    }
+    // -- O^T += V^T P^T: V^T rows 16m + r, keys 4q..4q+3 and 16+4q..16+4q+3 (two transposed reads)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int col = 16 * mt + 4 * (r % 4);
+      i16x4_t part[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int row = 16 * hf + 4 * q + r / 4;
+        const int posc = (col / 8) ^ (2 * (row % (D / 16)));
+        const uint32_t addr = vt_lds + row * ROWB + posc * 16 + (col % 8) * 2;
+        part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS i16x4_t*)(uintptr_t)addr);
+      }
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{
+          __builtin_bit_cast(u32x2_t, part[0])[0], __builtin_bit_cast(u32x2_t, part[0])[1],
+          __builtin_bit_cast(u32x2_t, part[1])[0], __builtin_bit_cast(u32x2_t, part[1])[1]});
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[nt], o[nt][mt], 0, 0, 0);
+    }
+  };
+
+  // ---- key blocks through two LDS buffers
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bool more = kb + 1 < nkb;
+    if (more) load_block(kb + 1);
+    if (!CAUSAL || kb * KB <= wave_hi) compute(kb, kb & 1);
+    if (more) store_block((kb + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store the wave's rows
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float lsum = wave_sum_xor_16_32(l_run[nt]);
+    if (pos[nt] >= p.S) continue;
+    OutT* orow = static_cast<OutT*>(p.out) + (((size_t)b * p.Hq + head[nt]) * p.S + pos[nt]) * D;
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) store_out4(orow + 16 * mt + 4 * q, o[nt][mt] * inv);
+  }
+}
+
+}  // namespace gqa

@@ -168,6 +168,30 @@ uint64_t gqa_kv_bytes_per_token(uint32_t layers, uint32_t kv_heads, uint32_t hea
                                 uint32_t dtype_bytes);
 
 /* ------------------------------------------------------------------------------------------------
+ * Prefill.  Attention of a whole prompt of S tokens over itself, the scaled_dot_product_attention
+ * call with enable_gqa (and is_causal) of "Grouped Query Attention: Why 8 KV Heads Decide Your Batch
+ * Size", section "Why doesn't GQA speed up my fine-tuned model?":
+ *
+ *     out[b,h,i,:] = sum_{t < n_i} softmax_t(scale * dot(q[b,h,i,:], k[b,j,t,:])) * v[b,j,t,:],
+ *     j = floor(h / G), n_i = i + 1 when causal, S otherwise.
+ *
+ * Layout (device memory, 16-byte aligned): q [B, Hq, S, d], k and v [B, Hkv, S, d] (bf16), out
+ * [B, Hq, S, d] (bf16 rounded to nearest even, or f32).  Each K/V tile is read once per workgroup and
+ * serves the G query heads of its group; nothing is expanded to Hq heads.  Supported: d in {64, 128},
+ * G a power of two up to 32.  No workspace.  Enqueued on `stream`; asynchronous.
+ */
+typedef struct {
+  int32_t B, Hq, Hkv, S, d;
+  int32_t dtype;     /* of q, k, v: GQA_BF16 */
+  int32_t out_dtype; /* GQA_BF16 or GQA_F32 */
+  int32_t causal;    /* 1: position i sees positions <= i; 0: every position */
+} gqa_prefill_shape_t;
+
+gqa_status_t gqa_prefill_shape_check(const gqa_prefill_shape_t* shape);
+gqa_status_t gqa_prefill(const void* q, const void* k, const void* v, float scale, void* out,
+                         const gqa_prefill_shape_t* shape, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * Serving planners (host only, no HIP call).
  *
  * Tensor-parallel head sharding ("Grouped Query Attention: Why 8 KV Heads Decide Your Batch Size",

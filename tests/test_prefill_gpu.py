@@ -1,0 +1,85 @@
+"""GPU parity of the prefill kernel (gqa_prefill) against the fp64 oracle, through the C ABI.
+
+bf16 inputs with fp32 accumulation; the weights are rounded to bf16 before P V, as in decode, so the
+bf16 gates apply (1e-2 absolute, and relative to the reference's scale).
+"""
+import numpy as np
+import pytest
+import torch
+
+import grouped_query_attention_04_amd as gqa
+import workloads
+from oracle import ref
+from tests.test_parity_gpu import DEV, compare, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run(case, causal=True, out_dtype=torch.bfloat16):
+    out = gqa.prefill(case["q"].to(DEV), case["k"].to(DEV), case["v"].to(DEV), case["scale"],
+                      out_dtype=out_dtype, causal=causal)
+    torch.cuda.synchronize()
+    return out
+
+
+SMALL = [
+    # (B, Hq, Hkv, S, d)
+    (1, 4, 1, 70, 64),       # G = 4, ragged last query block
+    (2, 8, 2, 129, 128),     # G = 4
+    (1, 2, 2, 300, 64),      # G = 1: 256 positions per workgroup, waves on different positions
+    (2, 4, 2, 200, 128),     # G = 2
+    (1, 16, 2, 100, 128),    # G = 8
+    (1, 16, 1, 33, 64),      # G = 16
+    (1, 32, 1, 60, 128),     # G = 32: a 16-row tile spans two heads
+    (1, 8, 8, 1, 128),       # a one-token prompt
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: "B{}Hq{}Hkv{}S{}d{}".format(*c))
+def test_prefill_small_parity(cfg, causal):
+    B, Hq, Hkv, S, d = cfg
+    say(f"prefill parity {cfg} causal={causal}")
+    case = workloads.make_prefill_case(B, Hq, Hkv, d, S, seed=hash(cfg) % 10000)
+    want = ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", causal)
+    compare(run(case, causal), want, "bf16", "bf16 out")
+    compare(run(case, causal, torch.float32), want, "bf16", "f32 out")
+
+
+def test_prefill_first_position_is_its_value_row_and_last_is_the_decode():
+    say("prefill: position 0 and position S-1")
+    B, Hq, Hkv, S, d = 2, 16, 4, 300, 128
+    case = workloads.make_prefill_case(B, Hq, Hkv, d, S, seed=91)
+    out = run(case, out_dtype=torch.float32).cpu()
+    G = Hq // Hkv
+    for h in range(Hq):
+        assert torch.allclose(out[:, h, 0], case["v"][:, h // G, 0].float(), atol=0, rtol=0)
+    dec = gqa.decode(case["q"][:, :, S - 1].contiguous().to(DEV), case["k"].to(DEV), case["v"].to(DEV),
+                     torch.full((B,), S, dtype=torch.int32, device=DEV), case["scale"],
+                     out_dtype=torch.float32).cpu()
+    assert (out[:, :, S - 1] - dec).abs().max() < 2e-3
+
+
+def test_prefill_is_deterministic():
+    case = workloads.make_prefill_case(1, 32, 8, 128, 777, seed=92)
+    a, b = run(case), run(case)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["prefill-8b", "prefill-70b"])
+def test_prefill_workload_parity(name):
+    """Full-size prefill workloads; the oracle checks sampled (b, h, i) rows: first and last
+    positions, both ends of every query block boundary sampled, and random rows."""
+    w = workloads.PREFILL_WORKLOADS[name]
+    say(f"prefill workload {name}: {w.name}")
+    case = workloads.make_prefill(name)
+    got = run(case).cpu()
+    rng = np.random.default_rng(93)
+    BM = 256 // w.G
+    rows = {(0, 0, 0), (w.B - 1, w.Hq - 1, w.S - 1), (0, w.G - 1, BM - 1), (0, w.G, BM), (w.B - 1, 1, w.S - 2)}
+    while len(rows) < 40:
+        rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.S))))
+    rows = sorted(rows)
+    want = ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", True, rows=rows)
+    sel = torch.stack([got[b, h, i] for b, h, i in rows])
+    compare(sel, want, "bf16", f"{name} {len(rows)} rows")

@@ -143,6 +143,52 @@ def paginate(case: dict, block_size: int, seed: int = 0, spare_pages: int = 0,
     return out
 
 
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    S: int
+    seed: int
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def flops(self) -> int:
+        """Causal prefill matmul flops: 2 * d for Q K^T and 2 * d for P V per (head, query, visible key)."""
+        return 4 * self.d * self.B * self.Hq * self.S * (self.S + 1) // 2
+
+
+# Prefill shapes: the scaled_dot_product_attention example's q [b, 32, s, 128] / kv [b, 8, s, 128]
+# (an 8B-class layer) and the 70B-class grouping (64 query heads, 8 KV heads).
+PREFILL_WORKLOADS = {
+    "prefill-8b": PrefillWorkload("prefill llama3-8b-layer B2 Hq32 Hkv8 d128 S4096", 2, 32, 8, 128, 4096, seed=1101),
+    "prefill-70b": PrefillWorkload("prefill llama-70b-layer B1 Hq64 Hkv8 d128 S8192", 1, 64, 8, 128, 8192, seed=1102),
+}
+
+
+def make_prefill_case(B: int, Hq: int, Hkv: int, d: int, S: int, seed: int = 0) -> dict:
+    """q [B,Hq,S,d], k and v [B,Hkv,S,d]: float32 standard normals drawn in that order from a CPU
+    generator seeded with `seed`, cast to bf16 with round-to-nearest-even."""
+    g = torch.Generator().manual_seed(int(seed))
+    q = torch.randn(B, Hq, S, d, generator=g, dtype=torch.float32)
+    k = torch.randn(B, Hkv, S, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, Hkv, S, d, generator=g, dtype=torch.float32)
+    return {"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16), "v": v.to(torch.bfloat16),
+            "scale": 1.0 / math.sqrt(d), "B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "d": d}
+
+
+def make_prefill(name: str) -> dict:
+    w = PREFILL_WORKLOADS[name]
+    case = make_prefill_case(w.B, w.Hq, w.Hkv, w.d, w.S, w.seed)
+    case["workload"] = w
+    return case
+
+
 def make(wid, seed: Optional[int] = None) -> dict:
     """Inputs of one named workload (ids 1, 2, 3, '4-mha', '4-gqa', '4-mqa', 5)."""
     w = WORKLOADS[wid]
