@@ -12,7 +12,9 @@
 
 namespace {
 
-constexpr int kWaves = 4;              // waves per workgroup
+constexpr int kWaves = 4;              // waves per workgroup (decode)
+constexpr int kPrefillWaves = 8;       // waves per prefill workgroup (256 rows: 16 * 16 / waves each)
+constexpr int kPrefillKeys = 64;       // keys per prefill LDS block
 constexpr int kDefaultWorkgroups = 256;  // one per compute unit of an MI355X
 constexpr int kMaxWorkgroups = 65536;
 constexpr size_t kAlign = 256;
@@ -390,17 +392,24 @@ gqa_status_t gqa_prefill(const void* q, const void* k, const void* v, float scal
   pp.qk_scale = (float)((double)scale * 1.4426950408889634);
   const unsigned grid = (unsigned)pp.nqb * (unsigned)(s->B * s->Hkv);
   hipStream_t hs = (hipStream_t)stream;
+  constexpr int NW = kPrefillWaves, NT = 16 / kPrefillWaves, KB = kPrefillKeys;
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, hs, pp);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), 0, hs, pp);
     return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
   };
   const bool bf = s->out_dtype == GQA_BF16;
   if (s->d == 64) {
-    if (s->causal) return bf ? go(gqa::prefill_mfma_kernel<64, uint16_t, true>) : go(gqa::prefill_mfma_kernel<64, float, true>);
-    return bf ? go(gqa::prefill_mfma_kernel<64, uint16_t, false>) : go(gqa::prefill_mfma_kernel<64, float, false>);
+    if (s->causal)
+      return bf ? go(gqa::prefill_mfma_kernel<64, uint16_t, true, NW, NT, KB>)
+                : go(gqa::prefill_mfma_kernel<64, float, true, NW, NT, KB>);
+    return bf ? go(gqa::prefill_mfma_kernel<64, uint16_t, false, NW, NT, KB>)
+              : go(gqa::prefill_mfma_kernel<64, float, false, NW, NT, KB>);
   }
-  if (s->causal) return bf ? go(gqa::prefill_mfma_kernel<128, uint16_t, true>) : go(gqa::prefill_mfma_kernel<128, float, true>);
-  return bf ? go(gqa::prefill_mfma_kernel<128, uint16_t, false>) : go(gqa::prefill_mfma_kernel<128, float, false>);
+  if (s->causal)
+    return bf ? go(gqa::prefill_mfma_kernel<128, uint16_t, true, NW, NT, KB>)
+              : go(gqa::prefill_mfma_kernel<128, float, true, NW, NT, KB>);
+  return bf ? go(gqa::prefill_mfma_kernel<128, uint16_t, false, NW, NT, KB>)
+            : go(gqa::prefill_mfma_kernel<128, float, false, NW, NT, KB>);
 }
 
 uint64_t gqa_kv_bytes_per_token(uint32_t layers, uint32_t kv_heads, uint32_t head_dim,

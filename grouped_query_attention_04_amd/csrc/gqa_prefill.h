@@ -9,7 +9,7 @@
 // Work decomposition.  A workgroup owns one (batch b, KV head j, block of BM query positions) and all
 // G query heads of the group, so every K/V tile it stages in LDS serves G heads at once -- the
 // grouping is used, not expanded (same page, the repeat_kv discussion).  Its 256 rows (G heads x BM
-// positions, BM = 256 / G) are split over 4 waves of 64 rows (four 16-row tiles).  Keys are taken
+// positions, BM = 256 / G) are split over NW waves of NT 16-row tiles each.  Keys are taken
 // in blocks of 32 through two LDS buffers: while the waves compute on one, the next block's loads
 // are in flight and land in the other.
 //
@@ -19,12 +19,23 @@
 //   O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with the 32 keys of the block as the contraction:
 //   k-slot 8q + e is key 4q + e (e < 4) or 16 + 4q + (e - 4) (e >= 4), so P^T's B operand is the
 //   lane's own eight probabilities, and A = V^T comes from two ds_read_b64_tr_b16 of the LDS V tile.
-//   Lane l holds O[row r][d = 16m + 4q + i]; the row's running max and sum live in the same lanes.
+//   Lane l holds O[row r][d = 16m + 4q + i]; the row's running max lives in the same lanes, and its
+//   running sum of (bf16) weights is one more PV product with an all-ones V^T tile.
+//   The running max is moved lazily: only when some row's block maximum exceeds it by more than 8
+//   (base 2) are the outputs rescaled, so weights stay below 2^8 and most blocks skip the rescale.
 #pragma once
 
 #include "gqa_kernels.h"
 
 namespace gqa {
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to a bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 
 struct PrefillParams {
   const void* q;  // [B][Hq][S][D] bf16
@@ -37,16 +48,20 @@ struct PrefillParams {
   float qk_scale; // scale * log2(e)
 };
 
-template <int D, typename OutT, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) prefill_mfma_kernel(PrefillParams p) {
-  constexpr int KB = 32;                // keys per block
-  constexpr int NT = 4;                 // 16-row tiles per wave
+template <int D, typename OutT, bool CAUSAL, int NW, int NT, int KB>
+__global__ void __launch_bounds__(NW * 64, 1) prefill_mfma_kernel(PrefillParams p) {
+  static_assert(NW * NT * 16 == 256, "a workgroup covers 256 rows");
+  static_assert(KB % 32 == 0, "keys per block: a multiple of 32");
+  constexpr int NTH = NW * 64;
+  constexpr int RW = 16 * NT;           // rows per wave
+  constexpr int NQ = KB / 16;           // 16-key quarters of a block (S^T tiles)
+  constexpr int NS = KB / 32;           // 32-key slabs of a block (PV contractions)
   constexpr int KS = D / 32;            // k-steps of QK^T
   constexpr int MT = D / 16;            // m-tiles of PV (head-dim columns)
   constexpr int ROWB = D * 2;           // bytes per K/V row
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILEB = KB * ROWB;      // bytes of one K (or V) block
-  constexpr int NLD = TILEB / 16 / 256; // 16-byte loads per thread per block and tensor
+  constexpr int NLD = (TILEB / 16 + NTH - 1) / NTH;  // 16-byte loads per thread per block and tensor
   __shared__ __attribute__((aligned(16))) char ks[2][TILEB];
   __shared__ __attribute__((aligned(16))) char vs[2][TILEB];
 
@@ -61,18 +76,18 @@ __global__ void __launch_bounds__(256, 1) prefill_mfma_kernel(PrefillParams p) {
   const int q = l / 16;
   const int r = l % 16;
 
-  // the wave's rows: row rho = 64 w + 16 nt + r is head g = rho / BM, position qb * BM + rho % BM
+  // the wave's rows: row rho = RW w + 16 nt + r is head g = rho / BM, position qb * BM + rho % BM
   int pos[NT];
   int head[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int rho = 64 * w + 16 * nt + r;
+    const int rho = RW * w + 16 * nt + r;
     head[nt] = j * p.G + (rho >> p.bm_shift);
     pos[nt] = qb * BM + (rho & (BM - 1));
   }
   // positions covered by the wave (for skipping blocks it cannot see) and by the workgroup
-  const int wave_lo = uniform(qb * BM + ((64 * w) & (BM - 1)));
-  const int wave_hi = uniform(min(p.S - 1, wave_lo + min(64, BM) - 1));
+  const int wave_lo = uniform(qb * BM + ((RW * w) & (BM - 1)));
+  const int wave_hi = uniform(min(p.S - 1, wave_lo + min(RW, BM) - 1));
   const int wg_hi = min(p.S, (qb + 1) * BM);  // exclusive
   const int nkb = CAUSAL ? (wg_hi + KB - 1) / KB : (p.S + KB - 1) / KB;
 
@@ -97,7 +112,8 @@ __global__ void __launch_bounds__(256, 1) prefill_mfma_kernel(PrefillParams p) {
   auto load_block = [&](int kb) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const uint32_t off = (uint32_t)kb * TILEB + (threadIdx.x + 256 * u) * 16;
+      const int idx = threadIdx.x + NTH * u;
+      const uint32_t off = idx < TILEB / 16 ? (uint32_t)kb * TILEB + idx * 16 : kNoTile;
       ldk[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
       ldv[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
@@ -106,30 +122,33 @@ __global__ void __launch_bounds__(256, 1) prefill_mfma_kernel(PrefillParams p) {
   auto store_block = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int idx = threadIdx.x + 256 * u;
+      const int idx = threadIdx.x + NTH * u;
+      if (idx >= TILEB / 16) break;
       const int row = idx / CPR, ch = idx % CPR;
       *reinterpret_cast<u32x4_t*>(ks[buf] + row * ROWB + ((ch ^ (row % CPR)) * 16)) = ldk[u];
       *reinterpret_cast<u32x4_t*>(vs[buf] + row * ROWB + ((ch ^ (2 * (row % (D / 16)))) * 16)) = ldv[u];
     }
   };
 
-  float m_run[NT], l_run[NT];
+  float m_run[NT];      // reference maximum per row, base-2 scaled domain
+  f32x4_t lsum[NT];     // running sum of the weights (every element holds the row's sum)
   f32x4_t o[NT][MT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
+    lsum[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
   auto compute = [&](int kb, int buf) {
     const char* kt_lds = ks[buf];
     const uint32_t vt_lds = (uint32_t)(uintptr_t)(GQA_LDS char*)vs[buf];
-    // -- scores S^T for the two 16-key halves
-    f32x4_t sc[2][NT];
+    // -- scores S^T for the 16-key quarters
+    f32x4_t sc[NQ][NT];
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < NQ; ++hf) {
       bf16x8_t ak[KS];
       const int row = 16 * hf + r;
 #pragma unroll
@@ -142,14 +161,14 @@ __global__ void __launch_bounds__(256, 1) prefill_mfma_kernel(PrefillParams p) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[s], bq[nt][s], acc, 0, 0, 0);
-        sc[hf][nt] = acc * p.qk_scale;
+        sc[hf][nt] = acc;  // unscaled: the scale is applied in the exponent
       }
     }
     // -- masks: keys past the prompt, and (causal) keys after the row's position
     const int k0 = kb * KB;
     if ((CAUSAL && k0 + KB - 1 > wave_lo) || k0 + KB > p.S) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+      for (int hf = 0; hf < NQ; ++hf)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + 16 * hf + 4 * q + i;
@@ -159,43 +178,49 @@ __global__ void __launch_bounds__(256, 1) prefill_mfma_kernel(PrefillParams p) {
         }
     }
     // -- online softmax; P^T in the B-operand layout of PV (k-slot 8q + e, see the header)
-    bf16x8_t bp[NT];
+    bf16x8_t bp[NS][NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+      for (int hf = 0; hf < NQ; ++hf)
         mx = fmaxf(mx, fmaxf(fmaxf(sc[hf][nt][0], sc[hf][nt][1]), fmaxf(sc[hf][nt][2], sc[hf][nt][3])));
-      mx = wave_max_xor_16_32(mx);
-      const float m_new = fmaxf(m_run[nt], mx);
-      // a row that has seen no key yet (m_new = -inf) keeps alpha = 1 and gets p = 0
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
-      m_run[nt] = m_new;
-      uint32_t pk[4];
-      float psum = 0.f;
+      const float mxs = wave_max_xor_16_32(mx) * p.qk_scale;
+      if (__any(mxs > m_run[nt] + 8.f)) {  // move the reference maximum (every lane of the wave)
+        const float m_new = fmaxf(m_run[nt], mxs);
+        // a row that has seen no key yet (m_new = -inf) keeps alpha = 1
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+        m_run[nt] = m_new;
+        lsum[nt] *= alpha;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+        for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+      }
+      const float neg_m = m_run[nt] == -INFINITY ? 0.f : -m_run[nt];
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2) {
-          const uint32_t lo = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[hf][nt][2 * i2] - m_use));
-          const uint32_t hi = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[hf][nt][2 * i2 + 1] - m_use));
-          psum += bf16_bits_to_float(lo) + bf16_bits_to_float(hi);
-          pk[2 * hf + i2] = lo | (hi << 16);
-        }
-      l_run[nt] = l_run[nt] * alpha + psum;
-      bp[nt] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+      for (int sl = 0; sl < NS; ++sl) {
+        uint32_t pk[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2) {
+            const f32x4_t& x = sc[2 * sl + h2][nt];
+            pk[2 * h2 + i2] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2], p.qk_scale, neg_m)),
+                                          __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2 + 1], p.qk_scale, neg_m)));
+          }
+        bp[sl][nt] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+        lsum[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bp[sl][nt], lsum[nt], 0, 0, 0);
+      }
     }
     // -- O^T += V^T P^T: V^T rows 16m + r, keys 4q..4q+3 and 16+4q..16+4q+3 (two transposed reads)
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int col = 16 * mt + 4 * (r % 4);
       i16x4_t part[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int row = 16 * hf + 4 * q + r / 4;
+        const int row = 32 * sl + 16 * hf + 4 * q + r / 4;
         const int posc = (col / 8) ^ (2 * (row % (D / 16)));
         const uint32_t addr = vt_lds + row * ROWB + posc * 16 + (col % 8) * 2;
         part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS i16x4_t*)(uintptr_t)addr);
@@ -204,7 +229,7 @@ __global__ void __launch_bounds__(256, 1) prefill_mfma_kernel(PrefillParams p) {
           __builtin_bit_cast(u32x2_t, part[0])[0], __builtin_bit_cast(u32x2_t, part[0])[1],
           __builtin_bit_cast(u32x2_t, part[1])[0], __builtin_bit_cast(u32x2_t, part[1])[1]});
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[nt], o[nt][mt], 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[sl][nt], o[nt][mt], 0, 0, 0);
     }
   };
 
@@ -223,10 +248,9 @@ __global__ void __launch_bounds__(256, 1) prefill_mfma_kernel(PrefillParams p) {
   // ---- normalise and store the wave's rows
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float lsum = wave_sum_xor_16_32(l_run[nt]);
     if (pos[nt] >= p.S) continue;
     OutT* orow = static_cast<OutT*>(p.out) + (((size_t)b * p.Hq + head[nt]) * p.S + pos[nt]) * D;
-    const float inv = 1.f / lsum;
+    const float inv = 1.f / lsum[nt][0];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) store_out4(orow + 16 * mt + 4 * q, o[nt][mt] * inv);
   }
