@@ -184,7 +184,7 @@ def main():
     ap.add_argument("--paged", type=int, default=0, metavar="BS",
                     help="lay the cache out in pages of BS positions (0 = dense cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-batches", type=int, default=16)
+    ap.add_argument("--cpu-sample-batches", type=int, default=32)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain torch copy of this many MiB (counter calibration)")
     args = ap.parse_args()

@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "gqa.h"
+#include "gqa_append.h"
 #include "gqa_kernels.h"
 #include "gqa_prefill.h"
 
