@@ -10,19 +10,25 @@
 // G query heads of the group, so every K/V tile it stages in LDS serves G heads at once -- the
 // grouping is used, not expanded (same page, the repeat_kv discussion).  Its 256 rows (G heads x BM
 // positions, BM = 256 / G) are split over NW waves of NT 16-row tiles each.  Keys are taken
-// in blocks of 32 through two LDS buffers: while the waves compute on one, the next block's loads
+// in blocks of KB through two LDS buffers: while the waves compute on one, the next block's loads
 // are in flight and land in the other.
 //
 // Per block and wave (lane l, quad q = l / 16, r = l % 16):
-//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16, two 16-key halves; A = K rows from LDS, B = the wave's
-//   query rows (registers).  Lane l holds S[row r][key 16h + 4q + i].
-//   O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with the 32 keys of the block as the contraction:
-//   k-slot 8q + e is key 4q + e (e < 4) or 16 + 4q + (e - 4) (e >= 4), so P^T's B operand is the
-//   lane's own eight probabilities, and A = V^T comes from two ds_read_b64_tr_b16 of the LDS V tile.
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16, one product per 16-key quarter; A = K rows from LDS,
+//   B = the wave's query rows (registers).  Lane l holds S[row r][key 16h + 4q + i] of quarter h.
+//   O^T += V^T P^T on v_mfma_f32_16x16x32_bf16 with each 32-key slab as the contraction: k-slot
+//   8q + e is key 4q + e (e < 4) or 16 + 4q + (e - 4) (e >= 4) of the slab, so P^T's B operand is
+//   the lane's own eight probabilities, and A = V^T comes from two ds_read_b64_tr_b16 of the V tile.
 //   Lane l holds O[row r][d = 16m + 4q + i]; the row's running max lives in the same lanes, and its
 //   running sum of (bf16) weights is one more PV product with an all-ones V^T tile.
 //   The running max is moved lazily: only when some row's block maximum exceeds it by more than 8
 //   (base 2) are the outputs rescaled, so weights stay below 2^8 and most blocks skip the rescale.
+//
+// Latency.  Each wave reads the K fragments of the next 16-key quarter, and all V^T fragments of a
+// slab, before it issues the products that use them, so one LDS round trip is paid per group of
+// products rather than per product.  The kernel declares its real occupancy (two waves per SIMD:
+// one 512-thread workgroup per CU), so that the compiler spends the registers on that read-ahead
+// instead of squeezing for an occupancy the workgroup size cannot reach.
 #pragma once
 
 #include "gqa_kernels.h"
@@ -31,6 +37,21 @@ namespace gqa {
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Maximum over the four lanes l, l^16, l^32, l^48 (the four quads holding one matrix column).
+// v_permlane16_swap(x, x) hands back x of rows {0,0,2,2} and {1,1,3,3} (rows of 16 lanes), and
+// v_permlane32_swap(x, x) x of halves {0,0} and {1,1}: the larger of each pair pairs lane l with
+// l^16, respectively l^32, without a trip through LDS.  Every lane ends with the same value.  The
+// maximum propagates NaN (a NaN score makes NaN weights either way) and so needs no quieting of its
+// operands.
+__device__ __forceinline__ float quad_max_permlane(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, x);
+  const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)c[0]), __builtin_bit_cast(float, (uint32_t)c[1]));
+}
 
 // Two floats to a bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -49,7 +70,8 @@ struct PrefillParams {
 };
 
 template <int D, typename OutT, bool CAUSAL, int NW, int NT, int KB>
-__global__ void __launch_bounds__(NW * 64, 1) prefill_mfma_kernel(PrefillParams p) {
+__global__ void __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+prefill_mfma_kernel(PrefillParams p) {
   static_assert(NW * NT * 16 == 256, "a workgroup covers 256 rows");
   static_assert(KB % 32 == 0, "keys per block: a multiple of 32");
   constexpr int NTH = NW * 64;
@@ -108,25 +130,35 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_mfma_kernel(PrefillParams 
   const size_t head_off = ((size_t)b * p.Hkv + j) * (size_t)p.S * ROWB;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(p.k) + head_off, (uint32_t)p.S * ROWB);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(p.v) + head_off, (uint32_t)p.S * ROWB);
-  u32x4_t ldk[NLD], ldv[NLD];
-  auto load_block = [&](int kb) {
-#pragma unroll
-    for (int u = 0; u < NLD; ++u) {
-      const int idx = threadIdx.x + NTH * u;
-      const uint32_t off = idx < TILEB / 16 ? (uint32_t)kb * TILEB + idx * 16 : kNoTile;
-      ldk[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      ldv[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
-    }
-  };
   // LDS placement: K chunk c of key row x at chunk c ^ (x % CPR); V as in the decode kernel's tile
-  auto store_block = [&](int buf) {
+  auto store_k = [&](char* dst, const u32x4_t* src) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int idx = threadIdx.x + NTH * u;
       if (idx >= TILEB / 16) break;
       const int row = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<u32x4_t*>(ks[buf] + row * ROWB + ((ch ^ (row % CPR)) * 16)) = ldk[u];
-      *reinterpret_cast<u32x4_t*>(vs[buf] + row * ROWB + ((ch ^ (2 * (row % (D / 16)))) * 16)) = ldv[u];
+      *reinterpret_cast<u32x4_t*>(dst + row * ROWB + ((ch ^ (row % CPR)) * 16)) = src[u];
+    }
+  };
+  auto store_v = [&](char* dst, const u32x4_t* src) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = threadIdx.x + NTH * u;
+      if (idx >= TILEB / 16) break;
+      const int row = idx / CPR, ch = idx % CPR;
+      *reinterpret_cast<u32x4_t*>(dst + row * ROWB + ((ch ^ (2 * (row % (D / 16)))) * 16)) = src[u];
+    }
+  };
+  auto chunk_off = [&](int blk, int u) __attribute__((always_inline)) {
+    const int idx = threadIdx.x + NTH * u;
+    return idx < TILEB / 16 ? (uint32_t)blk * TILEB + idx * 16 : kNoTile;
+  };
+  u32x4_t ldk[NLD], ldv[NLD];
+  auto load_block = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      ldk[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, chunk_off(kb, u), 0, 0));
+      ldv[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, chunk_off(kb, u), 0, 0));
     }
   };
 
@@ -141,30 +173,48 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_mfma_kernel(PrefillParams 
     for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  // Lane parts of the LDS read addresses; quarter, slab and half add compile-time offsets.
+  // K: quarter h, k-step s reads chunk (4s + q) of key row 16h + r, stored at chunk (4s + q) ^ (r % CPR).
+  // V^T: slab sl, half hf, m-tile mt reads columns 16mt + 4(r % 4) .. + 3 of key row
+  // 32sl + 16hf + 4q + r / 4, whose row index modulo D / 16 does not depend on sl or hf.
+  uint32_t koff[KS], voff[MT];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) koff[s] = r * ROWB + (((4 * s + q) ^ (r % CPR)) * 16);
+  {
+    const int vrow = 4 * q + r / 4;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int col = 16 * mt + 4 * (r % 4);
+      voff[mt] = vrow * ROWB + (((col / 8) ^ (2 * (vrow % (D / 16)))) * 16) + (col % 8) * 2;
+    }
+  }
+  f32x4_t sc[NQ][NT];   // scores S^T of the block in flight
+  bf16x8_t bp[NS][NT];  // its weights P^T in the B-operand layout of PV (k-slot 8q + e, see the header)
 
-  auto compute = [&](int kb, int buf) {
-    const char* kt_lds = ks[buf];
-    const uint32_t vt_lds = (uint32_t)(uintptr_t)(GQA_LDS char*)vs[buf];
-    // -- scores S^T for the 16-key quarters
-    f32x4_t sc[NQ][NT];
+  // -- S^T = K Q^T for the 16-key quarters of the block in LDS buffer kt_lds
+  auto qk = [&](const char* kt_lds) __attribute__((always_inline)) {
+    bf16x8_t ak[2][KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) ak[0][s] = *reinterpret_cast<const bf16x8_t*>(kt_lds + koff[s]);
 #pragma unroll
     for (int hf = 0; hf < NQ; ++hf) {
-      bf16x8_t ak[KS];
-      const int row = 16 * hf + r;
+      if (hf + 1 < NQ) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int ch = 4 * s + q;
-        ak[s] = *reinterpret_cast<const bf16x8_t*>(kt_lds + row * ROWB + ((ch ^ (row % CPR)) * 16));
+        for (int s = 0; s < KS; ++s)
+          ak[(hf + 1) & 1][s] = *reinterpret_cast<const bf16x8_t*>(kt_lds + 16 * (hf + 1) * ROWB + koff[s]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // the next quarter's reads are in flight during these products
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[s], bq[nt][s], acc, 0, 0, 0);
+        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak[hf & 1][s], bq[nt][s], acc, 0, 0, 0);
         sc[hf][nt] = acc;  // unscaled: the scale is applied in the exponent
       }
     }
-    // -- masks: keys past the prompt, and (causal) keys after the row's position
+  };
+  // -- masks, online softmax (lazy rescale of o and lsum), weights P^T of block kb
+  auto softmax = [&](int kb) __attribute__((always_inline)) {
     const int k0 = kb * KB;
     if ((CAUSAL && k0 + KB - 1 > wave_lo) || k0 + KB > p.S) {
 #pragma unroll
@@ -177,15 +227,14 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_mfma_kernel(PrefillParams 
             if (key >= p.S || (CAUSAL && key > pos[nt])) sc[hf][nt][i] = -INFINITY;
         }
     }
-    // -- online softmax; P^T in the B-operand layout of PV (k-slot 8q + e, see the header)
-    bf16x8_t bp[NS][NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float mx = -INFINITY;
+      float mx = -INFINITY;  // NaN-propagating, as in quad_max_permlane
 #pragma unroll
       for (int hf = 0; hf < NQ; ++hf)
-        mx = fmaxf(mx, fmaxf(fmaxf(sc[hf][nt][0], sc[hf][nt][1]), fmaxf(sc[hf][nt][2], sc[hf][nt][3])));
-      const float mxs = wave_max_xor_16_32(mx) * p.qk_scale;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_maximum(mx, sc[hf][nt][i]);
+      const float mxs = quad_max_permlane(mx) * p.qk_scale;
       if (__any(mxs > m_run[nt] + 8.f)) {  // move the reference maximum (every lane of the wave)
         const float m_new = fmaxf(m_run[nt], mxs);
         // a row that has seen no key yet (m_new = -inf) keeps alpha = 1
@@ -208,40 +257,57 @@ __global__ void __launch_bounds__(NW * 64, 1) prefill_mfma_kernel(PrefillParams 
                                           __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2 + 1], p.qk_scale, neg_m)));
           }
         bp[sl][nt] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
-        lsum[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bp[sl][nt], lsum[nt], 0, 0, 0);
       }
     }
-    // -- O^T += V^T P^T: V^T rows 16m + r, keys 4q..4q+3 and 16+4q..16+4q+3 (two transposed reads)
+  };
+  // -- O^T += V^T P^T and the row sums, for the block whose V is in LDS buffer vt: V^T rows 16m + r,
+  // keys 4q..4q+3 and 16+4q..16+4q+3 of each 32-key slab (two transposed reads)
+  auto pv = [&](const char* vt) __attribute__((always_inline)) {
+    const uint32_t vt_lds = (uint32_t)(uintptr_t)(GQA_LDS const char*)vt;
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl)
+    for (int sl = 0; sl < NS; ++sl) {
+      bf16x8_t av[MT];  // read ahead of the products, so that the LDS latency is paid once per slab
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int col = 16 * mt + 4 * (r % 4);
-      i16x4_t part[2];
+      for (int mt = 0; mt < MT; ++mt) {
+        i16x4_t part[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int row = 32 * sl + 16 * hf + 4 * q + r / 4;
-        const int posc = (col / 8) ^ (2 * (row % (D / 16)));
-        const uint32_t addr = vt_lds + row * ROWB + posc * 16 + (col % 8) * 2;
-        part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS i16x4_t*)(uintptr_t)addr);
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint32_t addr = vt_lds + (32 * sl + 16 * hf) * ROWB + voff[mt];
+          part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS i16x4_t*)(uintptr_t)addr);
+        }
+        av[mt] = __builtin_bit_cast(bf16x8_t, u32x4_t{
+            __builtin_bit_cast(u32x2_t, part[0])[0], __builtin_bit_cast(u32x2_t, part[0])[1],
+            __builtin_bit_cast(u32x2_t, part[1])[0], __builtin_bit_cast(u32x2_t, part[1])[1]});
       }
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, u32x4_t{
-          __builtin_bit_cast(u32x2_t, part[0])[0], __builtin_bit_cast(u32x2_t, part[0])[1],
-          __builtin_bit_cast(u32x2_t, part[1])[0], __builtin_bit_cast(u32x2_t, part[1])[1]});
+      __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bp[sl][nt], o[nt][mt], 0, 0, 0);
+      for (int nt = 0; nt < NT; ++nt) lsum[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bp[sl][nt], lsum[nt], 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mt], bp[sl][nt], o[nt][mt], 0, 0, 0);
     }
   };
 
-  // ---- key blocks through two LDS buffers
+  // ---- key blocks through two LDS buffers: block kb + 1 is loaded into registers while block kb is
+  // computed, then stored into the other buffer
   load_block(0);
-  store_block(0);
+  store_k(ks[0], ldk);
+  store_v(vs[0], ldv);
   __syncthreads();
   for (int kb = 0; kb < nkb; ++kb) {
+    const int buf = kb & 1;
     const bool more = kb + 1 < nkb;
     if (more) load_block(kb + 1);
-    if (!CAUSAL || kb * KB <= wave_hi) compute(kb, kb & 1);
-    if (more) store_block((kb + 1) & 1);
+    if (!CAUSAL || kb * KB <= wave_hi) {
+      qk(ks[buf]);
+      softmax(kb);
+      pv(vs[buf]);
+    }
+    if (more) {
+      store_k(ks[1 - buf], ldk);
+      store_v(vs[1 - buf], ldv);
+    }
     __syncthreads();
   }
 
