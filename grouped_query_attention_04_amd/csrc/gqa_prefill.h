@@ -31,6 +31,8 @@
 // instead of squeezing for an occupancy the workgroup size cannot reach.
 #pragma once
 
+#include <type_traits>
+
 #include "gqa_kernels.h"
 
 namespace gqa {
@@ -153,12 +155,13 @@ prefill_mfma_kernel(PrefillParams p) {
     const int idx = threadIdx.x + NTH * u;
     return idx < TILEB / 16 ? (uint32_t)blk * TILEB + idx * 16 : kNoTile;
   };
-  u32x4_t ldk[NLD], ldv[NLD];
-  auto load_block = [&](int kb) __attribute__((always_inline)) {
+  u32x4_t ldk[2][NLD], ldv[2][NLD];
+  auto load_block = [&](int kb, auto setc) __attribute__((always_inline)) {
+    constexpr int st = decltype(setc)::value;
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      ldk[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, chunk_off(kb, u), 0, 0));
-      ldv[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, chunk_off(kb, u), 0, 0));
+      ldk[st][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, chunk_off(kb, u), 0, 0));
+      ldv[st][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, chunk_off(kb, u), 0, 0));
     }
   };
 
@@ -217,15 +220,29 @@ prefill_mfma_kernel(PrefillParams p) {
   auto softmax = [&](int kb) __attribute__((always_inline)) {
     const int k0 = kb * KB;
     if ((CAUSAL && k0 + KB - 1 > wave_lo) || k0 + KB > p.S) {
+      if (CAUSAL) {
 #pragma unroll
-      for (int hf = 0; hf < NQ; ++hf)
+        for (int nt = 0; nt < NT; ++nt) {
+          // keys 16h + i of this lane's quarter columns are visible while 16h + i <= lim
+          const int lim = min(pos[nt], p.S - 1) - (k0 + 4 * q);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 16 * hf + 4 * q + i;
+          for (int hf = 0; hf < NQ; ++hf) {
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            if (key >= p.S || (CAUSAL && key > pos[nt])) sc[hf][nt][i] = -INFINITY;
+            for (int i = 0; i < 4; ++i)
+              if (16 * hf + i > lim) sc[hf][nt][i] = -INFINITY;
+            // four compares at a time: hoisting them all would hold a scalar register pair each
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < NQ; ++hf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (k0 + 16 * hf + 4 * q + i >= p.S)
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) sc[hf][nt][i] = -INFINITY;
+      }
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -289,26 +306,30 @@ prefill_mfma_kernel(PrefillParams p) {
     }
   };
 
-  // ---- key blocks through two LDS buffers: block kb + 1 is loaded into registers while block kb is
-  // computed, then stored into the other buffer
-  load_block(0);
-  store_k(ks[0], ldk);
-  store_v(vs[0], ldv);
+  // ---- key blocks through two LDS buffers, global loads two blocks ahead
+  load_block(0, std::integral_constant<int, 0>{});
+  if (1 < nkb) load_block(1, std::integral_constant<int, 1>{});
+  store_k(ks[0], ldk[0]);
+  store_v(vs[0], ldv[0]);
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    const bool more = kb + 1 < nkb;
-    if (more) load_block(kb + 1);
+  auto step = [&](int kb, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;  // kb % 2: block kb + 1 sits in set 1 - P, kb + 2 goes to set P
+    if (kb + 2 < nkb) load_block(kb + 2, par);
     if (!CAUSAL || kb * KB <= wave_hi) {
-      qk(ks[buf]);
+      qk(ks[P]);
       softmax(kb);
-      pv(vs[buf]);
+      pv(vs[P]);
     }
-    if (more) {
-      store_k(ks[1 - buf], ldk);
-      store_v(vs[1 - buf], ldv);
+    if (kb + 1 < nkb) {
+      store_k(ks[1 - P], ldk[1 - P]);
+      store_v(vs[1 - P], ldv[1 - P]);
     }
     __syncthreads();
+  };
+  for (int kb = 0; kb < nkb; kb += 2) {
+    step(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 >= nkb) break;
+    step(kb + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and store the wave's rows
