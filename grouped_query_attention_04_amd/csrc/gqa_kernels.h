@@ -198,6 +198,29 @@ __device__ __forceinline__ int range_owner(long long x, long long T, int weff) {
 
 template <int TILE, int NTH>
 __device__ bool find_range(const Params& p, Shared& sh, Range& r) {
+  if (p.B <= NTH) {
+    // One pass: thread b holds batch entry b's tile count; one scan gives the total and the
+    // entry's prefix, and the thread whose entry holds tile lo reports it.
+    const int b = (int)threadIdx.x;
+    const int t = b < p.B ? seq_tiles<TILE>(p, b) : 0;
+    int total;
+    const int incl = block_scan<NTH>(t, sh, &total);
+    r.T = (long long)p.Hkv * total;
+    r.weff = r.T < p.W ? (int)r.T : p.W;
+    const int w = blockIdx.x;
+    if (w >= r.weff) return false;
+    r.lo = range_lo(w, r.T, r.weff);
+    r.hi = range_lo(w + 1, r.T, r.weff);
+    const long long s = (long long)p.Hkv * (incl - t), e = (long long)p.Hkv * incl;
+    if (t > 0 && s <= r.lo && r.lo < e) {
+      sh.found_b = b;
+      sh.found_pre = incl - t;
+    }
+    __syncthreads();
+    r.b = uniform(sh.found_b);
+    r.pre = uniform(sh.found_pre);
+    return true;
+  }
   int part = 0;
   for (int b = threadIdx.x; b < p.B; b += NTH) part += seq_tiles<TILE>(p, b);
   r.T = (long long)p.Hkv * block_sum<NTH>(part, sh);
@@ -327,12 +350,18 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
   // below see what the other workgroups wrote through to memory.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  // Last piece of the segment: log-sum-exp merge of its pieces in workgroup order.  The piece loop
-  // is the outer (uniform) loop so that each piece's buffer descriptor stays scalar; every thread
-  // carries the running (max, sum, output) of its NI items, with the loads of PB pieces in flight.
+  // Last piece of the segment: log-sum-exp merge of its pieces in workgroup order.  Every thread
+  // carries the running (max, sum, output) of its NI items.  The pieces' partials stream through PB
+  // register sets: piece k is merged, then the loads of piece k + PB go out, so PB pieces are always
+  // in flight and the merge pays one load latency, not one per group of pieces.  The piece loop is
+  // uniform, so each piece's buffer descriptor stays scalar.
   constexpr int NI = (GT * D / 4 + NTH - 1) / NTH;
-  constexpr int PB = 4;
+  constexpr int PB = NI > 2 ? 4 : 8;  // pieces in flight (registers: 6 * NI per piece)
   const int npc = wlast - wfirst + 1;
+  // Slot of the segment's piece in workgroup w: workgroups after the first hold the segment from
+  // their first tile on, i.e. in slot 0; the first one holds it in slot 1 when the segment starts
+  // after its first tile.
+  const int first_slot = uniform(pc.s > range_lo(wfirst, r.T, r.weff) ? 1 : 0);
   float acc_m[NI], acc_l[NI];
   f32x4_t acc_o[NI];
 #pragma unroll
@@ -341,37 +370,45 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
     acc_l[i] = 0.f;
     acc_o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  for (int k0 = 0; k0 < npc; k0 += PB) {
-    float m[PB][NI], l[PB][NI];
-    u32x4_t o[PB][NI];
+  struct PieceRegs {
+    float m[NI], l[NI];
+    u32x4_t o[NI];
+  };
+  auto load_piece = [&](PieceRegs& R, int k) __attribute__((always_inline)) {
+    if (k >= npc) return;
+    const size_t sl = (size_t)uniform((wfirst + k) * 2 + (k == 0 ? first_slot : 0));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.part_o + sl * G * D, G * D * 4);
 #pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      const int w = wfirst + (k0 + u < npc ? k0 + u : 0);
-      // the segment's piece in workgroup w is its slot 1 only when the segment starts inside w's
-      // range, i.e. after w's first tile
-      const size_t sl = (size_t)uniform(w * 2 + (pc.s > range_lo(w, r.T, r.weff) ? 1 : 0));
-      const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.part_o + sl * G * D, G * D * 4);
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int item = tid + i * NTH;
-        const int g = (4 * (item < nitems ? item : 0)) / D;
-        m[u][i] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        l[u][i] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        o[u][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, item * 16, 0, kAgentScope));
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int item = tid + i * NTH;
+      if (i > 0 && uniform(i * NTH) >= nitems) break;  // item slots past the group's rows
+      const int g = (4 * (item < nitems ? item : 0)) / D;
+      R.m[i] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      R.l[i] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      R.o[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, item * 16, 0, kAgentScope));
     }
+  };
+  auto merge_piece = [&](const PieceRegs& R) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (i > 0 && uniform(i * NTH) >= nitems) break;  // not loaded: never stored either
+      const float mn = fmaxf(acc_m[i], R.m[i]);
+      const float a = __builtin_amdgcn_exp2f(acc_m[i] - mn);
+      const float sc = __builtin_amdgcn_exp2f(R.m[i] - mn);
+      acc_l[i] = acc_l[i] * a + R.l[i] * sc;
+      acc_o[i] = acc_o[i] * a + __builtin_bit_cast(f32x4_t, R.o[i]) * sc;
+      acc_m[i] = mn;
+    }
+  };
+  PieceRegs R[PB];
+#pragma unroll
+  for (int u = 0; u < PB; ++u) load_piece(R[u], u);
+  for (int k0 = 0; k0 < npc; k0 += PB) {
 #pragma unroll
     for (int u = 0; u < PB; ++u) {
       if (k0 + u >= npc) break;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float mn = fmaxf(acc_m[i], m[u][i]);
-        const float a = __builtin_amdgcn_exp2f(acc_m[i] - mn);
-        const float sc = __builtin_amdgcn_exp2f(m[u][i] - mn);
-        acc_l[i] = acc_l[i] * a + l[u][i] * sc;
-        acc_o[i] = acc_o[i] * a + __builtin_bit_cast(f32x4_t, o[u][i]) * sc;
-        acc_m[i] = mn;
-      }
+      merge_piece(R[u]);
+      load_piece(R[u], k0 + u + PB);
     }
   }
 #pragma unroll

@@ -65,6 +65,10 @@ WORKLOADS = {
                       seq_lens=(4096,) * 8, seed=1004),
     5: Workload("long-fp8 B2 Hq64 Hkv8 d128 L32768", 2, 64, 8, 128, 32768, "bf16", "fp8_e4m3",
                 seq_lens=(32768, 30000), seed=1005),
+    # one rank's share of the 70B-layer step under tensor parallelism of degree 8: one KV head and
+    # its 8 query heads per GPU; same seed, so the same sequence lengths as the whole step
+    "3-tp8": Workload("llama-70b-layer tp8-rank B32 Hq8 Hkv1 d128 L8192", 32, 8, 1, 128, 8192, "bf16", "bf16",
+                      seq_range=(6000, 8192), seed=1003),
 }
 
 
