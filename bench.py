@@ -35,7 +35,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of an MI355X
 TRAFFIC_SUMMARY = {0: os.path.join(ROOT, "profiles", "gqa_decode_llama70b_traffic.md"),
                    16: os.path.join(ROOT, "profiles", "gqa_decode_paged16_llama70b_traffic.md")}
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_attention_04_amd", "csrc", f)
-                  for f in ("gqa_kernels.h", "gqa_api.hip")]
+                  for f in ("gqa_device.h", "gqa_kernels.h", "gqa_api.hip")]
 
 
 def log(msg):

@@ -5,7 +5,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "gqa_api.hip"), os.path.join(PKG, "csrc", "gqa_plan.cpp")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("gqa_api.hip", "gqa_prefill_api.hip", "gqa_plan.cpp")]
 LIB = os.path.join(PKG, "libgqa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

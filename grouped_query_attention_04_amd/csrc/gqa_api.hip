@@ -1,5 +1,6 @@
-// gqa_api.hip -- host side of libgqa: argument validation, split-K planning, workspace layout and
-// kernel dispatch.  Every entry point declared in include/gqa.h is defined here.
+// gqa_api.hip -- host side of libgqa for decode, paged decode and cache append: argument validation,
+// split-K planning, workspace layout and kernel dispatch.  The prefill entry points are in
+// gqa_prefill_api.hip and the planners in gqa_plan.cpp.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -8,14 +9,16 @@
 
 #include "gqa.h"
 #include "gqa_append.h"
+#include "gqa_host.h"
 #include "gqa_kernels.h"
-#include "gqa_prefill.h"
 
 namespace {
 
+using gqa_host::aligned;
+using gqa_host::known_dtype;
+using gqa_host::log2_exact;
+
 constexpr int kWaves = 4;              // waves per workgroup (decode)
-constexpr int kPrefillWaves = 8;       // waves per prefill workgroup (256 rows: 16 * 16 / waves each)
-constexpr int kPrefillKeys = 64;       // keys per prefill LDS block
 constexpr int kDefaultWorkgroups = 256;  // one per compute unit of an MI355X
 constexpr int kMaxWorkgroups = 65536;
 constexpr size_t kAlign = 256;
@@ -23,7 +26,6 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int elt_bytes(int dt) { return dt == GQA_F32 ? 4 : dt == GQA_BF16 ? 2 : 1; }
-bool known_dtype(int dt) { return dt == GQA_F32 || dt == GQA_BF16 || dt == GQA_FP8_E4M3; }
 
 int plan_workgroups(const gqa_shape_t* s) {
   return s->num_workgroups > 0 ? s->num_workgroups : kDefaultWorkgroups;
@@ -51,8 +53,6 @@ Layout plan(const gqa_shape_t* s) {
   lo.total = lo.o_off + align_up(slots * G * (size_t)s->d * sizeof(float));
   return lo;
 }
-
-bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 template <typename K>
 gqa_status_t launch(K kernel, int grid, const gqa::Params& prm, hipStream_t stream) {
@@ -147,12 +147,6 @@ gqa_status_t launch_append(int new_dtype, int kv_dtype, int d, int B, const gqa:
                    : dispatch_append_kv<128, float, PAGED>(kv_dtype, B, ap, st);
   return d == 64 ? dispatch_append_kv<64, uint16_t, PAGED>(kv_dtype, B, ap, st)
                  : dispatch_append_kv<128, uint16_t, PAGED>(kv_dtype, B, ap, st);
-}
-
-int log2_exact(int x) {
-  int k = 0;
-  while ((1 << k) < x) ++k;
-  return (1 << k) == x ? k : -1;
 }
 
 template <int D, int GT>
@@ -351,66 +345,6 @@ gqa_status_t gqa_append_kv_paged(const void* k_new, const void* v_new, int32_t n
   ap.max_blocks = s->max_blocks;
   ap.num_blocks = s->num_blocks;
   return launch_append<true>(new_dtype, s->kv_dtype, s->d, s->B, ap, (hipStream_t)stream);
-}
-
-gqa_status_t gqa_prefill_shape_check(const gqa_prefill_shape_t* s) {
-  if (!s) return GQA_ERR_INVALID_ARG;
-  if (s->B <= 0 || s->Hq <= 0 || s->Hkv <= 0 || s->S <= 0 || s->d <= 0) return GQA_ERR_INVALID_ARG;
-  if (s->Hq % s->Hkv != 0) return GQA_ERR_INVALID_ARG;
-  if (!known_dtype(s->dtype) || !known_dtype(s->out_dtype)) return GQA_ERR_INVALID_ARG;
-  if (s->causal != 0 && s->causal != 1) return GQA_ERR_INVALID_ARG;
-  if (s->dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
-  if (s->out_dtype != GQA_BF16 && s->out_dtype != GQA_F32) return GQA_ERR_UNSUPPORTED;
-  if (s->d != 64 && s->d != 128) return GQA_ERR_UNSUPPORTED;
-  const int shift = log2_exact(s->Hq / s->Hkv);
-  if (shift < 0 || shift > 5) return GQA_ERR_UNSUPPORTED;  // G a power of two, at most 32
-  // per-(batch, KV head) K/V slices are addressed with 32-bit byte offsets
-  if ((long long)s->S * s->d * 2 >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
-  const long long nqb = ((long long)s->S * (s->Hq / s->Hkv) + 255) / 256;
-  if (nqb * s->B * s->Hkv >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
-  return GQA_OK;
-}
-
-gqa_status_t gqa_prefill(const void* q, const void* k, const void* v, float scale, void* out,
-                         const gqa_prefill_shape_t* s, void* stream) {
-  if (!q || !k || !v || !out || !s) return GQA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return GQA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
-  const gqa_status_t st = gqa_prefill_shape_check(s);
-  if (st != GQA_OK) return st;
-  gqa::PrefillParams pp;
-  pp.q = q;
-  pp.k = k;
-  pp.v = v;
-  pp.out = out;
-  pp.B = s->B;
-  pp.Hq = s->Hq;
-  pp.Hkv = s->Hkv;
-  pp.S = s->S;
-  pp.G = s->Hq / s->Hkv;
-  pp.bm_shift = 8 - log2_exact(pp.G);  // BM * G = 256 rows per workgroup
-  pp.nqb = (s->S + (1 << pp.bm_shift) - 1) >> pp.bm_shift;
-  pp.qk_scale = (float)((double)scale * 1.4426950408889634);
-  const unsigned grid = (unsigned)pp.nqb * (unsigned)(s->B * s->Hkv);
-  hipStream_t hs = (hipStream_t)stream;
-  constexpr int NW = kPrefillWaves, NT = 16 / kPrefillWaves, KB = kPrefillKeys;
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(NW * 64), 0, hs, pp);
-    return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
-  };
-  const bool bf = s->out_dtype == GQA_BF16;
-  if (s->d == 64) {
-    if (s->causal)
-      return bf ? go(gqa::prefill_mfma_kernel<64, uint16_t, true, NW, NT, KB>)
-                : go(gqa::prefill_mfma_kernel<64, float, true, NW, NT, KB>);
-    return bf ? go(gqa::prefill_mfma_kernel<64, uint16_t, false, NW, NT, KB>)
-              : go(gqa::prefill_mfma_kernel<64, float, false, NW, NT, KB>);
-  }
-  if (s->causal)
-    return bf ? go(gqa::prefill_mfma_kernel<128, uint16_t, true, NW, NT, KB>)
-              : go(gqa::prefill_mfma_kernel<128, float, true, NW, NT, KB>);
-  return bf ? go(gqa::prefill_mfma_kernel<128, uint16_t, false, NW, NT, KB>)
-            : go(gqa::prefill_mfma_kernel<128, float, false, NW, NT, KB>);
 }
 
 uint64_t gqa_kv_bytes_per_token(uint32_t layers, uint32_t kv_heads, uint32_t head_dim,

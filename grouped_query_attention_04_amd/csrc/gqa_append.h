@@ -1,7 +1,7 @@
 // gqa_append.h -- HIP kernel (gfx950) that writes the new token's K and V rows into the cache.
 #pragma once
 
-#include "gqa_kernels.h"
+#include "gqa_device.h"
 
 namespace gqa {
 

@@ -33,7 +33,7 @@
 
 #include <type_traits>
 
-#include "gqa_kernels.h"
+#include "gqa_device.h"
 
 namespace gqa {
 
@@ -68,7 +68,9 @@ struct PrefillParams {
   int B, Hq, Hkv, S, G;
   int bm_shift;   // BM = 1 << bm_shift query positions per workgroup (BM * G = 256 rows)
   int nqb;        // query blocks per (b, j)
-  float qk_scale; // scale * log2(e)
+  float qk_scale; // |scale| * log2(e), positive (1 * log2(e) for a zero scale)
+  uint32_t q_and; // applied to each 32-bit word (two bf16) of q: all ones, or 0 for a zero scale
+  uint32_t q_xor; // then: 0, or 0x80008000 (both signs) for a negative scale
 };
 
 template <int D, typename OutT, bool CAUSAL, int NW, int NT, int KB>
@@ -124,6 +126,9 @@ prefill_mfma_kernel(PrefillParams p) {
     for (int s = 0; s < KS; ++s) {
       u32x4_t v = {0, 0, 0, 0};
       if (pos[nt] < p.S) v = *reinterpret_cast<const u32x4_t*>(qr + 32 * s + 8 * q);
+      // the scale's sign goes into q (exact), so the multiplier below is positive and a row's
+      // largest raw score is its largest scaled score
+      v = (v & p.q_and) ^ p.q_xor;
       bq[nt][s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -166,11 +171,13 @@ prefill_mfma_kernel(PrefillParams p) {
   };
 
   float m_run[NT];      // reference maximum per row, base-2 scaled domain
+  float neg_m[NT];      // -m_run, or 0 while the row has seen no key (the exponent's offset)
   f32x4_t lsum[NT];     // running sum of the weights (every element holds the row's sum)
   f32x4_t o[NT][MT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m_run[nt] = -INFINITY;
+    neg_m[nt] = 0.f;
     lsum[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -246,22 +253,23 @@ prefill_mfma_kernel(PrefillParams p) {
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+      // This lane's maximum decides whether the reference moves (some score of the wave more than
+      // 8 above its row's reference); only then is the row maximum reduced across the quads.
       float mx = -INFINITY;  // NaN-propagating, as in quad_max_permlane
 #pragma unroll
       for (int hf = 0; hf < NQ; ++hf)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_maximum(mx, sc[hf][nt][i]);
-      const float mxs = quad_max_permlane(mx) * p.qk_scale;
-      if (__any(mxs > m_run[nt] + 8.f)) {  // move the reference maximum (every lane of the wave)
-        const float m_new = fmaxf(m_run[nt], mxs);
+      if (__any(mx * p.qk_scale > m_run[nt] + 8.f)) {  // move the reference maximum (every lane)
+        const float m_new = fmaxf(m_run[nt], quad_max_permlane(mx) * p.qk_scale);
         // a row that has seen no key yet (m_new = -inf) keeps alpha = 1
         const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
         m_run[nt] = m_new;
+        neg_m[nt] = m_new == -INFINITY ? 0.f : -m_new;
         lsum[nt] *= alpha;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
       }
-      const float neg_m = m_run[nt] == -INFINITY ? 0.f : -m_run[nt];
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl) {
         uint32_t pk[4];
@@ -270,8 +278,8 @@ prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
           for (int i2 = 0; i2 < 2; ++i2) {
             const f32x4_t& x = sc[2 * sl + h2][nt];
-            pk[2 * h2 + i2] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2], p.qk_scale, neg_m)),
-                                          __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2 + 1], p.qk_scale, neg_m)));
+            pk[2 * h2 + i2] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2], p.qk_scale, neg_m[nt])),
+                                          __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * i2 + 1], p.qk_scale, neg_m[nt])));
           }
         bp[sl][nt] = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
       }

@@ -130,3 +130,23 @@ def test_prefill_pins_accept_correct_definition():
 @pytest.mark.parametrize("mistake", ["interleaved_heads", "no_diagonal", "one_ahead", "no_mask"])
 def test_prefill_pins_reject_planted_mistake(mistake):
     assert not _prefill_pins_pass(lambda *a: _numpy_prefill(*a, mistake=mistake))
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0])
+def test_nonpositive_scales(scale):
+    """A negative scale is |scale| on -q (negation is exact), pinned to torch's SDPA in that form (its
+    fp64 math path returns NaN for a negative or zero scale under the causal mask); a zero scale
+    weighs every visible key the same, so each row is the mean of the visible value rows."""
+    q, k, v = _rand(1, 4, 2, 17, 8, "f32", seed=9)
+    for causal in (True, False):
+        got = ref.prefill(q, k, v, scale, "f32", causal)
+        if scale < 0:
+            want = torch.nn.functional.scaled_dot_product_attention(-q.double(), k.double(), v.double(),
+                                                                    is_causal=causal, enable_gqa=True,
+                                                                    scale=-scale)
+            np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-13)
+        else:
+            vv = v.double().repeat_interleave(2, dim=1)
+            n = torch.arange(1, 18, dtype=torch.float64)[:, None]
+            mean = vv.cumsum(2) / n if causal else vv.mean(2, keepdim=True).expand_as(vv)
+            np.testing.assert_allclose(got, mean.numpy(), rtol=0, atol=1e-14)

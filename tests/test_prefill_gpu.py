@@ -83,3 +83,25 @@ def test_prefill_workload_parity(name):
     want = ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", True, rows=rows)
     sel = torch.stack([got[b, h, i] for b, h, i in rows])
     compare(sel, want, "bf16", f"{name} {len(rows)} rows")
+
+
+@pytest.mark.parametrize("scale", [-0.11, -1.0, 0.0, -0.0])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_nonpositive_scales(scale, causal):
+    """Any finite scale is a valid call: a negative one flips the order of the scores, and zero
+    makes every visible key weigh the same (the mean of the visible value rows)."""
+    say(f"prefill scale {scale} causal={causal}")
+    B, Hq, Hkv, S, d = 2, 8, 2, 150, 128
+    case = workloads.make_prefill_case(B, Hq, Hkv, d, S, seed=93)
+    case["scale"] = scale
+    got = run(case, causal, torch.float32)
+    want = ref.prefill(case["q"], case["k"], case["v"], scale, "bf16", causal)
+    compare(got, want, "bf16", f"scale {scale}")
+    if scale == 0.0:
+        v = case["v"].double()
+        G = Hq // Hkv
+        n = torch.arange(1, S + 1, dtype=torch.float64)[:, None]
+        mean = v.cumsum(2) / n if causal else v.mean(2, keepdim=True).expand_as(v)
+        mean = mean.repeat_interleave(G, dim=1)
+        # the weights are exactly 1 (bf16), so only the fp32 accumulation order separates the two
+        assert (got.cpu().double() - mean).abs().max() < 1e-5
