@@ -124,3 +124,11 @@ def test_paged_workload_parity(wid, bs):
     if bad:
         say(f"  rows off the oracle: {bad}")
     compare(sel, want, w.kv_dtype, f"paged workload {wid} {len(rows)} rows")
+
+
+def test_paged_negative_scale():
+    say("paged decode, negative scale")
+    case = workloads.make_case(2, 16, 4, 128, 400, "bf16", "bf16", seq_lens=(400, 131), seed=15)
+    case["scale"] = -0.2
+    pg = workloads.paginate(case, 32, seed=16)
+    compare(run_paged(case, pg), oracle_paged(case, pg), "bf16", "paged scale -0.2")

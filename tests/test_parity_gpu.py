@@ -368,3 +368,13 @@ def test_workload_parity(wid):
     if bad:
         say(f"  rows off the oracle: {bad}; seq_lens {case['seq_lens'].tolist()}")
     compare(sel, want, w.kv_dtype, f"workload {wid} {len(rows)} rows")
+
+
+@pytest.mark.parametrize("qd,kd", DTYPES)
+@pytest.mark.parametrize("scale", [-0.13, 0.0])
+def test_nonpositive_scales(qd, kd, scale):
+    """Any finite scale is a valid call: a negative one reverses the order of the scores, and zero
+    weighs every cached position the same."""
+    say(f"decode scale {scale} q={qd} kv={kd}")
+    case = workloads.make_case(3, 16, 4, 128, 900, qd, kd, seq_lens=(900, 517, 3), seed=14)
+    compare(run(case, out_dtype="f32", scale=scale), oracle_full(case, scale=scale), kd, f"scale {scale}")
