@@ -10,8 +10,9 @@
 // G query heads of the group, so every K/V tile it stages in LDS serves G heads at once -- the
 // grouping is used, not expanded (same page, the repeat_kv discussion).  Its 256 rows (G heads x BM
 // positions, BM = 256 / G) are split over NW waves of NT 16-row tiles each.  Keys are taken
-// in blocks of KB through two LDS buffers: while the waves compute on one, the next block's loads
-// are in flight and land in the other.
+// in blocks of KB through two LDS buffers: while the waves compute on one block, the next one is
+// being stored into the other, and the global loads of the block after it are in flight in
+// registers.
 //
 // Per block and wave (lane l, quad q = l / 16, r = l % 16):
 //   S^T = K Q^T on v_mfma_f32_16x16x32_bf16, one product per 16-key quarter; A = K rows from LDS,
@@ -21,8 +22,10 @@
 //   the lane's own eight probabilities, and A = V^T comes from two ds_read_b64_tr_b16 of the V tile.
 //   Lane l holds O[row r][d = 16m + 4q + i]; the row's running max lives in the same lanes, and its
 //   running sum of (bf16) weights is one more PV product with an all-ones V^T tile.
-//   The running max is moved lazily: only when some row's block maximum exceeds it by more than 8
-//   (base 2) are the outputs rescaled, so weights stay below 2^8 and most blocks skip the rescale.
+//   The running max is moved lazily: only when some score of the wave exceeds its row's reference
+//   by more than 8 (base 2) are the row maxima reduced and the outputs rescaled, so weights stay
+//   below 2^8 and most blocks skip both.  The scale's sign is folded into q by the launcher, so the
+//   multiplier applied in the exponent is positive and raw-score maxima are scaled-score maxima.
 //
 // Latency.  Each wave reads the K fragments of the next 16-key quarter, and all V^T fragments of a
 // slab, before it issues the products that use them, so one LDS round trip is paid per group of
