@@ -292,7 +292,11 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=Non
     return out
 
 
-def _check_append(k_new, v_new, positions, tensors, B, Hkv, d):
+def _check_append(k_new, v_new, positions, tensors, B, Hkv, d, cache_dtype=None, skipped=None):
+    if cache_dtype is not None and cache_dtype not in _CODE:
+        raise TypeError(f"unsupported cache dtype {cache_dtype}")
+    if skipped is not None and (skipped.dtype != torch.int32 or skipped.numel() < 1):
+        raise ValueError("skipped must be an int32 tensor with at least one element")
     if k_new.shape != (B, Hkv, d) or v_new.shape != k_new.shape:
         raise ValueError("k_new and v_new must be [B, Hkv, d] matching the cache")
     if k_new.dtype not in (torch.float32, torch.bfloat16) or v_new.dtype != k_new.dtype:
@@ -313,9 +317,9 @@ def append_kv(k_new, v_new, k_cache, v_cache, positions, *, k_descale=1.0, v_des
     Positions past the cache add one to skipped (an int32 [1] device tensor) if given."""
     B, Hkv, L, d = k_cache.shape
     tensors = [k_new, v_new, k_cache, v_cache, positions] + ([skipped] if skipped is not None else [])
-    dev = _check_append(k_new, v_new, positions, tensors, B, Hkv, d)
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("k_cache and v_cache must match")
+    dev = _check_append(k_new, v_new, positions, tensors, B, Hkv, d, k_cache.dtype, skipped)
     q_code = F32 if k_cache.dtype == torch.float32 else BF16
     shape = make_shape(B, Hkv, Hkv, L, d, q_code, _CODE[k_cache.dtype], q_code, k_descale, v_descale)
     with torch.cuda.device(dev):
@@ -330,7 +334,9 @@ def append_kv_paged(k_new, v_new, k_pages, v_pages, block_table, positions, *, k
     num_blocks, Hkv, block_size, d = k_pages.shape
     B = positions.shape[0]
     tensors = [k_new, v_new, k_pages, v_pages, block_table, positions] + ([skipped] if skipped is not None else [])
-    dev = _check_append(k_new, v_new, positions, tensors, B, Hkv, d)
+    if v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
+        raise ValueError("k_pages and v_pages must match")
+    dev = _check_append(k_new, v_new, positions, tensors, B, Hkv, d, k_pages.dtype, skipped)
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be an int32 tensor of shape [B, max_blocks]")
     q_code = BF16

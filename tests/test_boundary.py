@@ -176,3 +176,21 @@ def test_paged_decode_rejects_before_any_hip_call():
     assert call(k=ctypes.c_void_p((1 << 20) + 8)) == 1
     assert call(shape=_paged(block_size=24)) == 2
     assert call(wsb=16) == 3
+
+
+def test_append_binding_rejects_bad_counter_and_cache_dtype():
+    """The binding checks these before touching a device (CPU tensors suffice)."""
+    import grouped_query_attention_04_amd as gqa
+    kn = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(2, 2, 8, 64, dtype=torch.bfloat16)
+    pos = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="skipped"):
+        gqa.append_kv(kn, kn, kc, kc, pos, skipped=torch.zeros(1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="skipped"):
+        gqa.append_kv(kn, kn, kc, kc, pos, skipped=torch.zeros(0, dtype=torch.int32))
+    with pytest.raises(TypeError, match="cache dtype"):
+        gqa.append_kv(kn, kn, kc.half(), kc.half(), pos)
+    pages = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
+    table = torch.zeros(2, 1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="must match"):
+        gqa.append_kv_paged(kn, kn, pages, pages[:2], table, pos)
