@@ -369,6 +369,8 @@ def prefill(q, k, v, scale=None, out=None, *, out_dtype=None, causal=True):
         raise ValueError("all tensors must be contiguous")
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.bfloat16
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"prefill writes bfloat16 or float32, not {out_dtype}")
     if out is None:
         out = torch.empty((B, Hq, S, d), dtype=out_dtype, device=dev)
     elif out.shape != (B, Hq, S, d) or out.dtype != out_dtype:
@@ -384,6 +386,8 @@ def prefill(q, k, v, scale=None, out=None, *, out_dtype=None, causal=True):
 
 def validate_seq_lens(seq_lens, L) -> int:
     """Number of entries outside [0, L] (synchronises)."""
+    if seq_lens.dtype != torch.int32 or seq_lens.device.type != "cuda" or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 CUDA (HIP) tensor")
     bad = torch.zeros(1, dtype=torch.int32, device=seq_lens.device)
     with torch.cuda.device(seq_lens.device):
         _check(lib.gqa_validate_seq_lens(seq_lens.data_ptr(), seq_lens.numel(), int(L),
@@ -393,6 +397,8 @@ def validate_seq_lens(seq_lens, L) -> int:
 
 def stream_read(src: torch.Tensor, sink: torch.Tensor = None):
     """Calibration read of every byte of src (non-temporal 16-byte loads)."""
+    if src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous CUDA (HIP) tensor")
     if sink is None:
         sink = torch.empty(lib.gqa_stream_read_sink_words(), dtype=torch.int32, device=src.device)
     nbytes = src.numel() * src.element_size()
