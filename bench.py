@@ -181,6 +181,8 @@ def main():
                     help="time causal prefill instead (prefill-8b or prefill-70b)")
     ap.add_argument("--append", action="store_true",
                     help="each step appends the new token's K/V rows before the decode")
+    ap.add_argument("--fused", action="store_true",
+                    help="with --append: one launch stores the new rows and decodes (gqa_decode_append)")
     ap.add_argument("--paged", type=int, default=0, metavar="BS",
                     help="lay the cache out in pages of BS positions (0 = dense cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -251,7 +253,24 @@ def main():
         positions = (sl - 1).clamp(min=-1).to(torch.int32).to(dev)
         ashape = shape
 
+    if args.fused and not args.append:
+        print("--fused times the fused append and decode: give --append too", file=sys.stderr)
+        return 2
+
     def step(i):
+        if args.fused:
+            if paged:
+                rc = gqa.lib.gqa_decode_append_paged(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(),
+                                                     kptr[i % copies], vptr[i % copies], table.data_ptr(),
+                                                     seq.data_ptr(), scale, out.data_ptr(), shape_ref, None,
+                                                     ws.data_ptr(), ws.numel(), sh)
+            else:
+                rc = gqa.lib.gqa_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), kptr[i % copies],
+                                               vptr[i % copies], seq.data_ptr(), scale, out.data_ptr(), shape_ref,
+                                               None, ws.data_ptr(), ws.numel(), sh)
+            if rc:
+                raise RuntimeError(gqa.status_string(rc))
+            return
         if args.append:
             if paged:
                 rc = gqa.lib.gqa_append_kv_paged(k_new.data_ptr(), v_new.data_ptr(), gqa.BF16, kptr[i % copies],
@@ -329,14 +348,16 @@ def main():
     traffic = recorded_traffic(wid, args.workgroups, args.paged)
     layout = f"paged, {args.paged} positions per page, random page placement" if paged else "dense"
     if args.append:
-        layout += "; each step appends the new token's K/V (bf16 rows) then decodes"
+        layout += ("; each step appends the new token's K/V (bf16 rows) and decodes, in one launch" if args.fused
+                   else "; each step appends the new token's K/V (bf16 rows) then decodes")
         traffic = None
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.kv_dtype, "data": "synthetic",
-        "config": {"workload": w.name + (f" paged bs{args.paged}" if paged else "") + (" append+decode" if args.append else ""),
+        "config": {"workload": w.name + (f" paged bs{args.paged}" if paged else "") + (
+                       (" fused append+decode" if args.fused else " append+decode") if args.append else ""),
                    "cache_layout": layout,
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L,
                    "seq_lens": f"sum {int(sl.sum())} (min {int(sl.min())}, max {int(sl.max())})",

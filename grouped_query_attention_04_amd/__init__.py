@@ -62,7 +62,8 @@ class PagedShape(ctypes.Structure):
 
 EXPORTS = ["gqa_shape_check", "gqa_decode_workspace_bytes", "gqa_workspace_init", "gqa_decode",
            "gqa_paged_shape_check", "gqa_decode_paged_workspace_bytes", "gqa_paged_workspace_init",
-           "gqa_decode_paged", "gqa_append_kv", "gqa_append_kv_paged", "gqa_prefill_shape_check",
+           "gqa_decode_paged", "gqa_append_kv", "gqa_append_kv_paged", "gqa_decode_append",
+           "gqa_decode_append_paged", "gqa_prefill_shape_check",
            "gqa_prefill", "gqa_tp_plan",
            "gqa_max_concurrency", "gqa_max_cached_tokens", "gqa_kv_bytes_per_token", "gqa_validate_seq_lens", "gqa_stream_read",
            "gqa_stream_read_sink_words", "gqa_status_string"]
@@ -95,6 +96,10 @@ def _load():
     lib.gqa_append_kv.restype = ctypes.c_int
     lib.gqa_append_kv_paged.argtypes = [vp, vp, i32, vp, vp, vp, pP, vp, vp, vp]
     lib.gqa_append_kv_paged.restype = ctypes.c_int
+    lib.gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, pS, vp, vp, sz, vp]
+    lib.gqa_decode_append.restype = ctypes.c_int
+    lib.gqa_decode_append_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, pP, vp, vp, sz, vp]
+    lib.gqa_decode_append_paged.restype = ctypes.c_int
     pF = ctypes.POINTER(PrefillShape)
     lib.gqa_prefill_shape_check.argtypes = [pF]
     lib.gqa_prefill_shape_check.restype = ctypes.c_int
@@ -214,6 +219,41 @@ def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, *, out_dtype=Non
     all contiguous CUDA tensors on one device.  Returns out [B,Hq,d] (dtype out_dtype, default q's).
     scale defaults to 1/sqrt(d).  num_workgroups (0 = library's choice) sets how many workgroups
     split the cache.  Enqueued on torch's current stream; no synchronisation."""
+    return _decode(q, k_cache, v_cache, seq_lens, scale, out, out_dtype, k_descale, v_descale,
+                   num_workgroups, workspace, None)
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, scale=None, out=None, *, out_dtype=None,
+                  k_descale=1.0, v_descale=1.0, num_workgroups=0, workspace=None, skipped=None):
+    """append_kv and decode in one launch.  k_new, v_new [B,Hkv,d] bf16 go to position
+    seq_lens[b] - 1 of the dense caches [B,Hkv,L,d] (bf16 or fp8-e4m3: the code of x / descale), and
+    the decode then attends over the first seq_lens[b] positions; q must be bf16.  The cache and the
+    output equal those of append_kv(positions=seq_lens - 1) followed by decode.  A new position past
+    the cache adds one to skipped (an int32 device tensor) if given.  Returns out."""
+    return _decode(q, k_cache, v_cache, seq_lens, scale, out, out_dtype, k_descale, v_descale,
+                   num_workgroups, workspace, (k_new, v_new, skipped))
+
+
+def _check_new_rows(new, B, Hkv, d):
+    k_new, v_new, skipped = new
+    if skipped is not None and (skipped.dtype != torch.int32 or skipped.numel() < 1):
+        raise ValueError("skipped must be an int32 tensor with at least one element")
+    if k_new.shape != (B, Hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [B, Hkv, d] matching the cache")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("the fused append takes bfloat16 new rows")
+    return [k_new, v_new] + ([skipped] if skipped is not None else [])
+
+
+def _new_ptrs(new):
+    if new is None:
+        return ()
+    k_new, v_new, skipped = new
+    return k_new.data_ptr(), v_new.data_ptr(), None if skipped is None else skipped.data_ptr()
+
+
+def _decode(q, k_cache, v_cache, seq_lens, scale, out, out_dtype, k_descale, v_descale, num_workgroups,
+            workspace, new):
     if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
         raise ValueError("expected q [B,Hq,d], k_cache and v_cache [B,Hkv,L,d]")
     if k_cache.dtype != v_cache.dtype:
@@ -224,6 +264,8 @@ def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, *, out_dtype=Non
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be an int32 tensor of shape [B]")
     tensors = [q, k_cache, v_cache, seq_lens] + ([out] if out is not None else [])
+    if new is not None:
+        tensors += _check_new_rows(new, B, k_cache.shape[1], d)
     dev = q.device
     if dev.type != "cuda" or any(t.device != dev for t in tensors):
         raise ValueError("all tensors must live on one CUDA (HIP) device")
@@ -240,9 +282,16 @@ def decode(q, k_cache, v_cache, seq_lens, scale=None, out=None, *, out_dtype=Non
     shape = _shape_from(q, k_cache, out_dtype, k_descale, v_descale, num_workgroups)
     ws = workspace if workspace is not None else workspace_for(shape, dev)
     with torch.cuda.device(dev):
-        _check(lib.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                              seq_lens.data_ptr(), float(scale), out.data_ptr(),
-                              ctypes.byref(shape), ws.data_ptr(), ws.numel(), _stream_handle(dev)))
+        if new is None:
+            _check(lib.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                  seq_lens.data_ptr(), float(scale), out.data_ptr(),
+                                  ctypes.byref(shape), ws.data_ptr(), ws.numel(), _stream_handle(dev)))
+        else:
+            kn, vn, sk = _new_ptrs(new)
+            _check(lib.gqa_decode_append(q.data_ptr(), kn, vn, k_cache.data_ptr(), v_cache.data_ptr(),
+                                         seq_lens.data_ptr(), float(scale), out.data_ptr(),
+                                         ctypes.byref(shape), sk, ws.data_ptr(), ws.numel(),
+                                         _stream_handle(dev)))
     return out
 
 
@@ -252,6 +301,22 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=Non
     [num_blocks,Hkv,block_size,d] (bf16 or fp8-e4m3); block_table [B,max_blocks] int32 (position t of
     sequence b is row t % block_size of page block_table[b, t // block_size]); seq_lens [B] int32.
     Returns out [B,Hq,d].  Enqueued on torch's current stream; no synchronisation."""
+    return _decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, out, out_dtype, k_descale,
+                         v_descale, num_workgroups, workspace, None)
+
+
+def decode_append_paged(q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, scale=None, out=None, *,
+                        out_dtype=None, k_descale=1.0, v_descale=1.0, num_workgroups=0, workspace=None,
+                        skipped=None):
+    """decode_append for a paged cache: append_kv_paged(positions=seq_lens - 1) and decode_paged in
+    one launch.  A new position past max_blocks * block_size, or on a page outside the pool, adds one
+    to skipped if given.  Returns out."""
+    return _decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, out, out_dtype, k_descale,
+                         v_descale, num_workgroups, workspace, (k_new, v_new, skipped))
+
+
+def _decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, out, out_dtype, k_descale, v_descale,
+                  num_workgroups, workspace, new):
     if q.dim() != 3 or k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
         raise ValueError("expected q [B,Hq,d], k_pages and v_pages [num_blocks,Hkv,block_size,d]")
     if k_pages.dtype != v_pages.dtype:
@@ -265,6 +330,8 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=Non
     if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,):
         raise ValueError("seq_lens must be an int32 tensor of shape [B]")
     tensors = [q, k_pages, v_pages, block_table, seq_lens] + ([out] if out is not None else [])
+    if new is not None:
+        tensors += _check_new_rows(new, B, Hkv, d)
     dev = q.device
     if dev.type != "cuda" or any(t.device != dev for t in tensors):
         raise ValueError("all tensors must live on one CUDA (HIP) device")
@@ -285,10 +352,17 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale=None, out=Non
                              v_descale, num_workgroups)
     ws = workspace if workspace is not None else workspace_for(shape, dev)
     with torch.cuda.device(dev):
-        _check(lib.gqa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
-                                    block_table.data_ptr(), seq_lens.data_ptr(), float(scale),
-                                    out.data_ptr(), ctypes.byref(shape), ws.data_ptr(), ws.numel(),
-                                    _stream_handle(dev)))
+        if new is None:
+            _check(lib.gqa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                        block_table.data_ptr(), seq_lens.data_ptr(), float(scale),
+                                        out.data_ptr(), ctypes.byref(shape), ws.data_ptr(), ws.numel(),
+                                        _stream_handle(dev)))
+        else:
+            kn, vn, sk = _new_ptrs(new)
+            _check(lib.gqa_decode_append_paged(q.data_ptr(), kn, vn, k_pages.data_ptr(), v_pages.data_ptr(),
+                                               block_table.data_ptr(), seq_lens.data_ptr(), float(scale),
+                                               out.data_ptr(), ctypes.byref(shape), sk, ws.data_ptr(),
+                                               ws.numel(), _stream_handle(dev)))
     return out
 
 

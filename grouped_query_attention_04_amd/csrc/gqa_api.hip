@@ -60,27 +60,27 @@ gqa_status_t launch(K kernel, int grid, const gqa::Params& prm, hipStream_t stre
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
-template <int D, int NT, bool FP8, bool PAGED>
+template <int D, int NT, bool FP8, bool PAGED, bool APPEND>
 gqa_status_t dispatch_mfma_out(int out_dtype, int grid, const gqa::Params& prm, hipStream_t st) {
   if (out_dtype == GQA_BF16)
-    return launch(gqa::decode_mfma_kernel<D, NT, FP8, uint16_t, kWaves, PAGED>, grid, prm, st);
-  return launch(gqa::decode_mfma_kernel<D, NT, FP8, float, kWaves, PAGED>, grid, prm, st);
+    return launch(gqa::decode_mfma_kernel<D, NT, FP8, uint16_t, kWaves, PAGED, APPEND>, grid, prm, st);
+  return launch(gqa::decode_mfma_kernel<D, NT, FP8, float, kWaves, PAGED, APPEND>, grid, prm, st);
 }
 
-template <int D, bool FP8, bool PAGED>
+template <int D, bool FP8, bool PAGED, bool APPEND>
 gqa_status_t dispatch_mfma(int G, int out_dtype, int grid, const gqa::Params& prm, hipStream_t st) {
-  if (G <= 16) return dispatch_mfma_out<D, 1, FP8, PAGED>(out_dtype, grid, prm, st);
-  return dispatch_mfma_out<D, 2, FP8, PAGED>(out_dtype, grid, prm, st);
+  if (G <= 16) return dispatch_mfma_out<D, 1, FP8, PAGED, APPEND>(out_dtype, grid, prm, st);
+  return dispatch_mfma_out<D, 2, FP8, PAGED, APPEND>(out_dtype, grid, prm, st);
 }
 
-template <bool PAGED>
+template <bool PAGED, bool APPEND = false>
 gqa_status_t dispatch_mfma_dtype(int kv_dtype, int d, int G, int out_dtype, int grid, const gqa::Params& prm,
                                  hipStream_t st) {
   if (kv_dtype == GQA_BF16)
-    return d == 64 ? dispatch_mfma<64, false, PAGED>(G, out_dtype, grid, prm, st)
-                   : dispatch_mfma<128, false, PAGED>(G, out_dtype, grid, prm, st);
-  return d == 64 ? dispatch_mfma<64, true, PAGED>(G, out_dtype, grid, prm, st)
-                 : dispatch_mfma<128, true, PAGED>(G, out_dtype, grid, prm, st);
+    return d == 64 ? dispatch_mfma<64, false, PAGED, APPEND>(G, out_dtype, grid, prm, st)
+                   : dispatch_mfma<128, false, PAGED, APPEND>(G, out_dtype, grid, prm, st);
+  return d == 64 ? dispatch_mfma<64, true, PAGED, APPEND>(G, out_dtype, grid, prm, st)
+                 : dispatch_mfma<128, true, PAGED, APPEND>(G, out_dtype, grid, prm, st);
 }
 
 // The dense shape that a paged shape's kernels and workspace are planned with: L is the longest
@@ -125,6 +125,11 @@ gqa::Params base_params(const void* q, const void* k, const void* v, const int32
   prm.block_shift = 0;
   prm.max_blocks = 0;
   prm.num_blocks = 0;
+  prm.k_new = nullptr;
+  prm.v_new = nullptr;
+  prm.skipped = nullptr;
+  prm.k_enc_descale = s->k_descale;
+  prm.v_enc_descale = s->v_descale;
   return prm;
 }
 
@@ -285,6 +290,72 @@ gqa_status_t gqa_decode_paged(const void* q, const void* k_pages, const void* v_
   prm.num_blocks = s->num_blocks;
   return dispatch_mfma_dtype<true>(s->kv_dtype, s->d, prm.G, s->out_dtype, lo.workgroups, prm,
                                    (hipStream_t)stream);
+}
+
+// Checks shared by the fused append-and-decode entry points: bf16 new rows, a bf16 or fp8 cache
+// (the matrix-core kernels), a bf16 query.
+static gqa_status_t fused_append_check(const void* k_new, const void* v_new, const int32_t* skipped,
+                                       int q_dtype, int kv_dtype) {
+  if (!k_new || !v_new) return GQA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || (skipped && !aligned(skipped, 4))) return GQA_ERR_INVALID_ARG;
+  if (q_dtype != GQA_BF16 || (kv_dtype != GQA_BF16 && kv_dtype != GQA_FP8_E4M3)) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+
+gqa_status_t gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                               void* v_cache, const int32_t* seq_lens, float scale, void* out,
+                               const gqa_shape_t* s, int32_t* skipped_count, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !out || !s) return GQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(seq_lens, 4))
+    return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  gqa_status_t st = gqa_shape_check(s);
+  if (st != GQA_OK) return st;
+  st = fused_append_check(k_new, v_new, skipped_count, s->q_dtype, s->kv_dtype);
+  if (st != GQA_OK) return st;
+  const Layout lo = plan(s);
+  if (!workspace || workspace_bytes < lo.total) return GQA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return GQA_ERR_INVALID_ARG;
+
+  gqa::Params prm = base_params(q, k_cache, v_cache, seq_lens, scale, out, s, lo, workspace);
+  prm.k_new = k_new;
+  prm.v_new = v_new;
+  prm.skipped = skipped_count;
+  return dispatch_mfma_dtype<false, true>(s->kv_dtype, s->d, prm.G, s->out_dtype, lo.workgroups, prm,
+                                          (hipStream_t)stream);
+}
+
+gqa_status_t gqa_decode_append_paged(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                                     void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                                     float scale, void* out, const gqa_paged_shape_t* s,
+                                     int32_t* skipped_count, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !out || !s) return GQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(out, 16) ||
+      !aligned(seq_lens, 4) || !aligned(block_table, 4))
+    return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  gqa_status_t st = gqa_paged_shape_check(s);
+  if (st != GQA_OK) return st;
+  st = fused_append_check(k_new, v_new, skipped_count, s->q_dtype, s->kv_dtype);
+  if (st != GQA_OK) return st;
+  const gqa_shape_t e = dense_equivalent(s);
+  const Layout lo = plan(&e);
+  if (!workspace || workspace_bytes < lo.total) return GQA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return GQA_ERR_INVALID_ARG;
+
+  gqa::Params prm = base_params(q, k_pages, v_pages, seq_lens, scale, out, &e, lo, workspace);
+  prm.block_table = block_table;
+  prm.block_shift = log2_exact(s->block_size);
+  prm.max_blocks = s->max_blocks;
+  prm.num_blocks = s->num_blocks;
+  prm.k_new = k_new;
+  prm.v_new = v_new;
+  prm.skipped = skipped_count;
+  return dispatch_mfma_dtype<true, true>(s->kv_dtype, s->d, prm.G, s->out_dtype, lo.workgroups, prm,
+                                         (hipStream_t)stream);
 }
 
 gqa_status_t gqa_append_kv(const void* k_new, const void* v_new, int32_t new_dtype, void* k_cache,

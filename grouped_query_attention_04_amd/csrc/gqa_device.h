@@ -15,6 +15,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 #define GQA_LDS __attribute__((address_space(3)))
+// Constant address space: a uniform read through it is a scalar load, which waits on no vector load.
+#define GQA_CONST __attribute__((address_space(4)))
 
 // Raw-buffer descriptor word 3 for gfx950 (32-bit data format, no swizzle, range checked).
 constexpr int kBufferFlags = 0x00020000;
@@ -92,6 +94,24 @@ template <>
 __device__ __forceinline__ void store_out4<uint16_t>(uint16_t* p, f32x4_t x) {
   *reinterpret_cast<u32x2_t*>(p) = u32x2_t{float_to_bf16_bits(x[0]) | (float_to_bf16_bits(x[1]) << 16),
                                            float_to_bf16_bits(x[2]) | (float_to_bf16_bits(x[3]) << 16)};
+}
+
+// e4m3fn code of x / descale: binary32 division, then round to nearest even, saturating at +-448
+// (infinities included); a NaN x gives 0x7F with its sign bit.
+__device__ __forceinline__ uint32_t float_to_fp8_e4m3_bits(float x, float descale) {
+  const uint32_t ux = __builtin_bit_cast(uint32_t, x);
+  if ((ux & 0x7fffffffu) > 0x7f800000u) return 0x7fu | ((ux >> 24) & 0x80u);  // NaN
+  const float y = __fdiv_rn(x, descale);
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x43e00000u) return 0x7eu | sign;  // |y| >= 448
+  if (a < 0x3c800000u) {                      // |y| < 2^-6: multiples of 2^-9 (8 is the smallest normal)
+    return sign | (uint32_t)__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f);
+  }
+  // keep three mantissa bits, rounding to nearest even, then move the exponent bias from 127 to 7
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+  return sign | (r - (120u << 3));
 }
 
 }  // namespace gqa

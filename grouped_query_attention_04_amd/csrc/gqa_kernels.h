@@ -42,7 +42,38 @@ struct Params {
   // [B][max_blocks]; block_size = 1 << block_shift positions per page.
   const int32_t* block_table;
   int block_shift, max_blocks, num_blocks;
+  // fused append (decode_mfma_kernel with APPEND): the new rows k_new, v_new [B][Hkv][D] (bf16) go
+  // to position seq_lens[b] - 1, in the cache format (fp8: code of x / enc_descale).
+  const void* k_new;
+  const void* v_new;
+  int32_t* skipped;  // optional: sequences whose new position lies past the cache or on a page outside the pool
+  float k_enc_descale, v_enc_descale;
 };
+
+// One 16-byte cache chunk of a new row from its bf16 source (SRC 16-byte words: one for a bf16
+// cache, two for fp8), converted as the cache-append kernel converts it.
+template <bool FP8>
+__device__ __forceinline__ u32x4_t encode_new_chunk(const u32x4_t* src, float descale) {
+  u32x4_t e;
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = src[0][i];
+      e[i] = float_to_bf16_bits(bf16_bits_to_float(w & 0xffffu)) |
+             (float_to_bf16_bits(bf16_bits_to_float(w >> 16)) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w0 = src[i / 2][2 * (i % 2)], w1 = src[i / 2][2 * (i % 2) + 1];
+      e[i] = float_to_fp8_e4m3_bits(bf16_bits_to_float(w0 & 0xffffu), descale) |
+             (float_to_fp8_e4m3_bits(bf16_bits_to_float(w0 >> 16), descale) << 8) |
+             (float_to_fp8_e4m3_bits(bf16_bits_to_float(w1 & 0xffffu), descale) << 16) |
+             (float_to_fp8_e4m3_bits(bf16_bits_to_float(w1 >> 16), descale) << 24);
+    }
+  }
+  return e;
+}
 
 // ------------------------------------------------------------------------------------------------
 // Tile space and its split over workgroups.
@@ -388,7 +419,7 @@ __device__ void for_each_piece(const Params& p, const Range& r, Body&& body) {
 // the set's own tile loads and moved to a scalar register when that tile is computed, after the
 // wait for the tile, so it never costs a wait of its own.  The page's buffer descriptors are built
 // per tile; a page number outside the pool yields a descriptor of zero bytes.
-template <int D, int NT, bool FP8, typename OutT, int NW, bool PAGED>
+template <int D, int NT, bool FP8, typename OutT, int NW, bool PAGED, bool APPEND>
 __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(Params p) {
   constexpr int TILE = 16;
   constexpr int NTH = NW * 64;
@@ -406,6 +437,12 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ Shared sh;
 
+  if constexpr (APPEND) {
+    // sequences whose new position lies past the cache: counted once, by workgroup b mod W
+    if (p.skipped && threadIdx.x == 0)
+      for (int b = blockIdx.x; b < p.B; b += p.W)
+        if (p.seq_lens[b] > p.L) __hip_atomic_fetch_add(p.skipped, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   zero_empty_rows<D, OutT, NTH>(p);
   Range rg;
   if (!find_range<TILE, NTH>(p, sh, rg)) return;
@@ -441,6 +478,38 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(p.k) + head, (uint32_t)n * ROWB);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(p.v) + head, (uint32_t)n * ROWB);
     const int mine = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;  // piece tiles w, w+NW, ...
+
+    // fused append: position ap = seq_lens[b] - 1 of this segment receives the new rows.  The wave
+    // that owns ap's tile loads the rows' bf16 source now; when it computes that tile it puts the
+    // rows, in the cache format, in place of the loaded ones and writes them to the cache.
+    constexpr int SRC = 2 / ELT;        // 16-byte source words per 16-byte cache chunk
+    constexpr int CPRB = ROWB / 16;     // 16-byte cache chunks per row
+    int ap_it = -1, ap_row = 0;         // the wave's iteration of ap's tile, and ap's row in it
+    u32x4_t nks[APPEND ? NK * SRC : 1], nvs[APPEND ? SRC : 1];
+    if constexpr (APPEND) {
+      const int raw = *(const GQA_CONST int32_t*)(uintptr_t)(p.seq_lens + pc.b);  // scalar load
+      const int ap = raw - 1;
+      const int rel = (ap >= 0 ? ap / TILE : 0) - tile0;
+      if (ap >= 0 && ap < p.L && rel >= 0 && rel < ntiles && rel % NW == w) {
+        ap_it = rel / NW;
+        ap_row = ap % TILE;
+        const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + ((size_t)pc.b * p.Hkv + pc.j) * D;
+        const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + ((size_t)pc.b * p.Hkv + pc.j) * D;
+        if (r == ap_row) {  // K: this lane holds row r, bytes x * 64 + q * 16 of chunk x
+#pragma unroll
+          for (int x = 0; x < NK; ++x)
+#pragma unroll
+            for (int c = 0; c < SRC; ++c)
+              nks[x * SRC + c] = *reinterpret_cast<const u32x4_t*>(kn + (x * 64 + q * 16) / ELT + 8 * c);
+        }
+        const int lv = (ap_row * CPRB) % 64;  // V: lanes lv .. lv + CPRB - 1 hold row ap_row's chunks
+        if (l >= lv && l < lv + CPRB) {
+#pragma unroll
+          for (int c = 0; c < SRC; ++c)
+            nvs[c] = *reinterpret_cast<const u32x4_t*>(vn + (l - lv) * 16 / ELT + 8 * c);
+        }
+      }
+    }
 
     // paged cache: this sequence's page-table row
     __amdgpu_buffer_rsrc_t rtab = rk;
@@ -499,6 +568,45 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
 
     auto compute = [&](Regs& R, int it) {
       const int t0 = tile_start(it);
+      if constexpr (APPEND) {
+        if (it == ap_it) {
+          // the new rows replace the loaded row ap_row of this tile and are written to the cache
+          __amdgpu_buffer_rsrc_t tk = rk, tv = rv;
+          uint32_t base = (uint32_t)t0;  // position of the tile's row 0 within the descriptors
+          bool ok = true;
+          if constexpr (PAGED) {
+            const int page = R.page;  // this tile's page (the entry for the set's next tile comes below)
+            ok = (uint32_t)page < (uint32_t)p.num_blocks;
+            const size_t pbase = (((size_t)page * p.Hkv + pc.j) << p.block_shift) * ROWB;
+            const uint32_t bytes = ok ? (uint32_t)ROWB << p.block_shift : 0u;
+            tk = make_rsrc(static_cast<const char*>(p.k) + pbase, bytes);
+            tv = make_rsrc(static_cast<const char*>(p.v) + pbase, bytes);
+            base &= (1u << p.block_shift) - 1;
+            // a page outside the pool is neither written nor patched (the tile reads zeros), and
+            // the sequence is counted once (by its first KV head)
+            if (!ok && pc.j == 0 && threadIdx.x % 64 == 0 && p.skipped)
+              __hip_atomic_fetch_add(p.skipped, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (ok) {
+            if (r == ap_row) {
+#pragma unroll
+              for (int x = 0; x < NK; ++x) {
+                const u32x4_t e = encode_new_chunk<FP8>(&nks[x * SRC], p.k_enc_descale);
+                R.k[x] = e;
+                __builtin_amdgcn_raw_buffer_store_b128(e, tk, (base + ap_row) * ROWB + x * 64 + q * 16, 0, 0);
+              }
+            }
+            const int lv = (ap_row * CPRB) % 64, xv = ap_row * CPRB / 64;
+            if (l >= lv && l < lv + CPRB) {
+              const u32x4_t e = encode_new_chunk<FP8>(nvs, p.v_enc_descale);
+#pragma unroll
+              for (int x = 0; x < NV; ++x)
+                if (x == xv) R.v[x] = e;
+              __builtin_amdgcn_raw_buffer_store_b128(e, tv, base * ROWB + (xv * 64 + l) * 16, 0, 0);
+            }
+          }
+        }
+      }
       if constexpr (PAGED) R.page = uniform(R.pg);  // loaded ahead of this tile's data
       // -- stage V (as bf16) into the wave's LDS tile, 16-byte chunks XOR-swizzled by row
 #pragma unroll

@@ -13,7 +13,8 @@
  * Efficient Multi-Head Attention", Worked example 2).  One decode step attends over the cached K/V
  * of the tokens already in the cache ("Grouped Query Attention (GQA): Efficient Multi-Head
  * Attention", section "The bottleneck: autoregressive decoding ..."); here those are exactly the first
- * seq_lens[b] positions of the cache, and appending the new token is the caller's job.  A sequence
+ * seq_lens[b] positions of the cache, and the new token's rows are stored by gqa_append_kv before
+ * the call (or by the fused gqa_decode_append entry points further down).  A sequence
  * with seq_lens[b] == 0 gets an all-zero output row.  The cache is read once per KV head for all G
  * query heads of its group; nothing is expanded to Hq heads ("Grouped Query Attention: Why 8 KV
  * Heads Decide Your Batch Size", sections "Why does GQA speed up decode, not just save memory?" and
@@ -160,6 +161,38 @@ gqa_status_t gqa_append_kv(const void* k_new, const void* v_new, int32_t new_dty
 gqa_status_t gqa_append_kv_paged(const void* k_new, const void* v_new, int32_t new_dtype, void* k_pages,
                                  void* v_pages, const int32_t* block_table, const gqa_paged_shape_t* shape,
                                  const int32_t* positions, int32_t* skipped_count, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Append fused into the decode.  One decoding step stores the new token's K and V rows and then
+ * attends over the cache that now holds them ("Grouped Query Attention (GQA): Efficient Multi-Head
+ * Attention", section "The bottleneck: autoregressive decoding is not attention's finest hour").
+ * These entry points do both in one launch: the result equals gqa_append_kv (new_dtype GQA_BF16,
+ * positions[b] = seq_lens[b] - 1) followed by gqa_decode (or gqa_decode_paged) with the same
+ * seq_lens, bit for bit, in both the cache and out.
+ *   - seq_lens[b] counts the new token: its rows k_new[b] and v_new[b] ([B, Hkv, d] bf16, 16-byte
+ *     aligned, device) go to position seq_lens[b] - 1 of sequence b, converted to the cache's format
+ *     as gqa_append_kv converts bf16 rows (fp8-e4m3 caches divide by the shape's k_descale and
+ *     v_descale), and the decode attends over positions [0, min(seq_lens[b], L)).
+ *   - seq_lens[b] <= 0 writes nothing (and the output row is zero, as in the decode).  seq_lens[b] > L
+ *     (L = max_blocks * block_size when paged) writes nothing, attends over all L positions and adds
+ *     one to *skipped_count; so does a new position whose page-table entry lies outside
+ *     [0, num_blocks) (that page then reads as zeros, as in gqa_decode_paged).  skipped_count is a
+ *     device int32 (4-byte aligned) or NULL.
+ *   - The cache is written at the new position only; the kernel that attends reads the new rows from
+ *     registers, so no ordering between the write and the read is needed.
+ *   - q_dtype must be GQA_BF16 and kv_dtype GQA_BF16 or GQA_FP8_E4M3 (else GQA_ERR_UNSUPPORTED);
+ *     out_dtype, the workspace and every other argument are as for gqa_decode / gqa_decode_paged,
+ *     with the same errors, returned before any HIP call.  Enqueued on `stream`; asynchronous.
+ */
+gqa_status_t gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                               void* v_cache, const int32_t* seq_lens, float scale, void* out,
+                               const gqa_shape_t* shape, int32_t* skipped_count, void* workspace,
+                               size_t workspace_bytes, void* stream);
+gqa_status_t gqa_decode_append_paged(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                                     void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                                     float scale, void* out, const gqa_paged_shape_t* shape,
+                                     int32_t* skipped_count, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /* KV-cache bytes per token: 2 (one K and one V tensor) * layers * kv_heads * head_dim * dtype_bytes
  * ("Grouped Query Attention: Why 8 KV Heads Decide Your Batch Size", section "Why does GQA decide

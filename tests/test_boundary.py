@@ -194,3 +194,60 @@ def test_append_binding_rejects_bad_counter_and_cache_dtype():
     table = torch.zeros(2, 1, dtype=torch.int32)
     with pytest.raises(ValueError, match="must match"):
         gqa.append_kv_paged(kn, kn, pages, pages[:2], table, pos)
+
+
+def _bf16(**kw):
+    return _shape(**dict(dict(q_dtype=gqa.BF16, kv_dtype=gqa.BF16), **kw))
+
+
+def test_fused_append_decode_rejects_before_any_hip_call():
+    good = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
+    odd = ctypes.c_void_p((1 << 20) + 8)
+
+    def dense(shape=None, wsb=1 << 30, **over):
+        a = dict(q=good, kn=good, vn=good, k=good, v=good, sl=good, out=good, sk=None, ws=good)
+        a.update(over)
+        return gqa.lib.gqa_decode_append(a["q"], a["kn"], a["vn"], a["k"], a["v"], a["sl"], 0.1, a["out"],
+                                         ctypes.byref(shape or _bf16()), a["sk"], a["ws"], wsb, None)
+
+    assert dense(kn=None) == 1
+    assert dense(vn=None) == 1
+    assert dense(kn=odd) == 1                                    # new rows must be 16-byte aligned
+    assert dense(sk=ctypes.c_void_p((1 << 20) + 2)) == 1          # counter must be 4-byte aligned
+    assert dense(shape=_shape(q_dtype=gqa.F32, kv_dtype=gqa.F32, out_dtype=gqa.F32)) == 2
+    assert dense(shape=_bf16(d=96)) == 2
+    assert dense(wsb=16) == 3
+    assert dense(ws=None) == 3
+
+    def paged(shape=None, wsb=1 << 30, **over):
+        a = dict(q=good, kn=good, vn=good, k=good, v=good, t=good, sl=good, out=good, sk=None, ws=good)
+        a.update(over)
+        return gqa.lib.gqa_decode_append_paged(a["q"], a["kn"], a["vn"], a["k"], a["v"], a["t"], a["sl"], 0.1,
+                                               a["out"], ctypes.byref(shape or _paged()), a["sk"], a["ws"],
+                                               wsb, None)
+
+    assert paged(t=None) == 1
+    assert paged(vn=None) == 1
+    assert paged(vn=odd) == 1
+    assert paged(shape=_paged(block_size=24)) == 2
+    assert paged(wsb=16) == 3
+
+
+def test_fused_append_binding_validates_new_rows():
+    """Checked before any device test, so CPU tensors reach these errors."""
+    q = torch.zeros(2, 8, 64, dtype=torch.bfloat16)
+    kc = torch.zeros(2, 2, 16, 64, dtype=torch.bfloat16)
+    kn = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
+    sl = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(TypeError, match="bfloat16"):
+        gqa.decode_append(q, kn.float(), kn.float(), kc, kc, sl)
+    with pytest.raises(ValueError, match="k_new and v_new"):
+        gqa.decode_append(q, kn[:, :1], kn[:, :1], kc, kc, sl)
+    with pytest.raises(ValueError, match="skipped"):
+        gqa.decode_append(q, kn, kn, kc, kc, sl, skipped=torch.zeros(1, dtype=torch.int64))
+    pages = torch.zeros(4, 2, 16, 64, dtype=torch.bfloat16)
+    table = torch.zeros(2, 1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="k_new and v_new"):
+        gqa.decode_append_paged(q, kn, kn[:1], pages, pages, table, sl)
+    with pytest.raises(ValueError):
+        gqa.decode_append_paged(q, kn, kn, pages, pages, table, sl)   # CPU tensors are refused
