@@ -290,9 +290,12 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
   }
   __syncthreads();
   if (!uniform(sh.last)) return;
-  // Acquire at agent scope: drop this XCD's cached copies of the workspace lines, so the loads
-  // below see what the other workgroups wrote through to memory.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // No acquire fence (it would invalidate this XCD's whole L2, about 2 us): every load of the other
+  // pieces below carries agent scope (sc1), the form of a relaxed agent-scope atomic load, which is
+  // coherent across the XCDs' L2 caches by itself; and each is issued after the counter update
+  // returned (thread 0 waited for it before the barrier), so it sees the stores the other
+  // workgroups completed before theirs.  The compiler fence keeps the loads below the barrier.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   // Last piece of the segment: log-sum-exp merge of its pieces in workgroup order.  Every thread
   // carries the running (max, sum, output) of its NI items.  The pieces' partials stream through PB
