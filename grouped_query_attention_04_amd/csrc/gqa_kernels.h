@@ -50,31 +50,6 @@ struct Params {
   float k_enc_descale, v_enc_descale;
 };
 
-// One 16-byte cache chunk of a new row from its bf16 source (SRC 16-byte words: one for a bf16
-// cache, two for fp8), converted as the cache-append kernel converts it.
-template <bool FP8>
-__device__ __forceinline__ u32x4_t encode_new_chunk(const u32x4_t* src, float descale) {
-  u32x4_t e;
-  if constexpr (!FP8) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w = src[0][i];
-      e[i] = float_to_bf16_bits(bf16_bits_to_float(w & 0xffffu)) |
-             (float_to_bf16_bits(bf16_bits_to_float(w >> 16)) << 16);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w0 = src[i / 2][2 * (i % 2)], w1 = src[i / 2][2 * (i % 2) + 1];
-      e[i] = float_to_fp8_e4m3_bits(bf16_bits_to_float(w0 & 0xffffu), descale) |
-             (float_to_fp8_e4m3_bits(bf16_bits_to_float(w0 >> 16), descale) << 8) |
-             (float_to_fp8_e4m3_bits(bf16_bits_to_float(w1 & 0xffffu), descale) << 16) |
-             (float_to_fp8_e4m3_bits(bf16_bits_to_float(w1 >> 16), descale) << 24);
-    }
-  }
-  return e;
-}
-
 // ------------------------------------------------------------------------------------------------
 // Tile space and its split over workgroups.
 
@@ -439,6 +414,8 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
   constexpr int SMEM = (NW * VTILE > Epi::kBytes) ? NW * VTILE : Epi::kBytes;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ Shared sh;
+  // fused append: per wave, the new K and V rows in the cache format (unused otherwise)
+  __shared__ __attribute__((aligned(16))) char ascr[APPEND ? NW * 2 * ROWB : 16];
 
   if constexpr (APPEND) {
     // sequences whose new position lies past the cache: counted once, by workgroup b mod W
@@ -483,12 +460,14 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
     const int mine = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;  // piece tiles w, w+NW, ...
 
     // fused append: position ap = seq_lens[b] - 1 of this segment receives the new rows.  The wave
-    // that owns ap's tile loads the rows' bf16 source now; when it computes that tile it puts the
-    // rows, in the cache format, in place of the loaded ones and writes them to the cache.
-    constexpr int SRC = 2 / ELT;        // 16-byte source words per 16-byte cache chunk
+    // that owns ap's tile loads the rows' bf16 source now, D / 64 elements of each row per lane;
+    // when it computes that tile it converts them to the cache format (spread over all lanes, as
+    // the fp8 conversion is long), gathers the 16-byte chunks each lane holds of row ap through
+    // LDS, puts them in place of the loaded ones and writes them to the cache.
+    constexpr int EPL = D / 64;         // elements of each new row per lane
     constexpr int CPRB = ROWB / 16;     // 16-byte cache chunks per row
     int ap_it = -1, ap_row = 0;         // the wave's iteration of ap's tile, and ap's row in it
-    u32x4_t nks[APPEND ? NK * SRC : 1], nvs[APPEND ? SRC : 1];
+    uint32_t kw = 0, vw = 0;            // this lane's source elements (bf16 bits) of the new rows
     if constexpr (APPEND) {
       const int raw = *(const GQA_CONST int32_t*)(uintptr_t)(p.seq_lens + pc.b);  // scalar load
       const int ap = raw - 1;
@@ -496,20 +475,13 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
       if (ap >= 0 && ap < p.L && rel >= 0 && rel < ntiles && rel % NW == w) {
         ap_it = rel / NW;
         ap_row = ap % TILE;
-        const uint16_t* kn = static_cast<const uint16_t*>(p.k_new) + ((size_t)pc.b * p.Hkv + pc.j) * D;
-        const uint16_t* vn = static_cast<const uint16_t*>(p.v_new) + ((size_t)pc.b * p.Hkv + pc.j) * D;
-        if (r == ap_row) {  // K: this lane holds row r, bytes x * 64 + q * 16 of chunk x
-#pragma unroll
-          for (int x = 0; x < NK; ++x)
-#pragma unroll
-            for (int c = 0; c < SRC; ++c)
-              nks[x * SRC + c] = *reinterpret_cast<const u32x4_t*>(kn + (x * 64 + q * 16) / ELT + 8 * c);
-        }
-        const int lv = (ap_row * CPRB) % 64;  // V: lanes lv .. lv + CPRB - 1 hold row ap_row's chunks
-        if (l >= lv && l < lv + CPRB) {
-#pragma unroll
-          for (int c = 0; c < SRC; ++c)
-            nvs[c] = *reinterpret_cast<const u32x4_t*>(vn + (l - lv) * 16 / ELT + 8 * c);
+        const size_t row = ((size_t)pc.b * p.Hkv + pc.j) * D;
+        if constexpr (EPL == 2) {
+          kw = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.k_new) + row)[l];
+          vw = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.v_new) + row)[l];
+        } else {
+          kw = static_cast<const uint16_t*>(p.k_new)[row + l];
+          vw = static_cast<const uint16_t*>(p.v_new)[row + l];
         }
       }
     }
@@ -587,25 +559,50 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
             base &= (1u << p.block_shift) - 1;
             // a page outside the pool is neither written nor patched (the tile reads zeros), and
             // the sequence is counted once (by its first KV head)
-            if (!ok && pc.j == 0 && threadIdx.x % 64 == 0 && p.skipped)
+            if (!ok && pc.j == 0 && l == 0 && p.skipped)
               __hip_atomic_fetch_add(p.skipped, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
           if (ok) {
-            if (r == ap_row) {
+            // this lane's elements in the cache format, into the wave's scratch: K row, then V row
+            uint32_t ek = 0, ev = 0;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) {
+              const float xk = bf16_bits_to_float((kw >> (16 * e)) & 0xffffu);
+              const float xv = bf16_bits_to_float((vw >> (16 * e)) & 0xffffu);
+              if constexpr (FP8) {
+                ek |= float_to_fp8_e4m3_bits(xk, p.k_enc_descale) << (8 * e);
+                ev |= float_to_fp8_e4m3_bits(xv, p.v_enc_descale) << (8 * e);
+              } else {
+                ek |= float_to_bf16_bits(xk) << (16 * e);
+                ev |= float_to_bf16_bits(xv) << (16 * e);
+              }
+            }
+            char* as = ascr + w * 2 * ROWB;
+            if constexpr (EPL * ELT == 4) {
+              *reinterpret_cast<uint32_t*>(as + 4 * l) = ek;
+              *reinterpret_cast<uint32_t*>(as + ROWB + 4 * l) = ev;
+            } else if constexpr (EPL * ELT == 2) {
+              *reinterpret_cast<uint16_t*>(as + 2 * l) = (uint16_t)ek;
+              *reinterpret_cast<uint16_t*>(as + ROWB + 2 * l) = (uint16_t)ev;
+            } else {
+              *reinterpret_cast<uint8_t*>(as + l) = (uint8_t)ek;
+              *reinterpret_cast<uint8_t*>(as + ROWB + l) = (uint8_t)ev;
+            }
+            if (r == ap_row) {  // K: this lane holds row r, bytes x * 64 + q * 16 of chunk x
 #pragma unroll
               for (int x = 0; x < NK; ++x) {
-                const u32x4_t e = encode_new_chunk<FP8>(&nks[x * SRC], p.k_enc_descale);
-                R.k[x] = e;
-                __builtin_amdgcn_raw_buffer_store_b128(e, tk, (base + ap_row) * ROWB + x * 64 + q * 16, 0, 0);
+                const u32x4_t c = *reinterpret_cast<const u32x4_t*>(as + x * 64 + q * 16);
+                R.k[x] = c;
+                __builtin_amdgcn_raw_buffer_store_b128(c, tk, (base + ap_row) * ROWB + x * 64 + q * 16, 0, 0);
               }
             }
             const int lv = (ap_row * CPRB) % 64, xv = ap_row * CPRB / 64;
-            if (l >= lv && l < lv + CPRB) {
-              const u32x4_t e = encode_new_chunk<FP8>(nvs, p.v_enc_descale);
+            if (l >= lv && l < lv + CPRB) {  // V: lanes lv .. lv + CPRB - 1 hold row ap_row's chunks
+              const u32x4_t c = *reinterpret_cast<const u32x4_t*>(as + ROWB + (l - lv) * 16);
 #pragma unroll
               for (int x = 0; x < NV; ++x)
-                if (x == xv) R.v[x] = e;
-              __builtin_amdgcn_raw_buffer_store_b128(e, tv, base * ROWB + (xv * 64 + l) * 16, 0, 0);
+                if (x == xv) R.v[x] = c;
+              __builtin_amdgcn_raw_buffer_store_b128(c, tv, base * ROWB + (xv * 64 + l) * 16, 0, 0);
             }
           }
         }
