@@ -15,6 +15,8 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 #define GQA_LDS __attribute__((address_space(3)))
 // Constant address space: a uniform read through it is a scalar load, which waits on no vector load.
@@ -50,6 +52,11 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u | ((u >> 16) & 0x8000u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// Two floats to a bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32; lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Two fp8-e4m3fn codes (the low or high 16 bits of `w`) -> two bf16 in one dword.  Exact: every

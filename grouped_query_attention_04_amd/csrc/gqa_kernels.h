@@ -652,28 +652,34 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) sc[nt][i] = -INFINITY;
       }
-      // -- online softmax; P^T packed to bf16 in the B-operand layout of PV
+      // -- online softmax with a lazy reference maximum: the weights are 2^(s - m_run), and m_run
+      //    moves (rescaling the row's sum and output) only when the row's tile maximum exceeds it
+      //    by more than 8, so weights stay below 2^8 and, past the first tiles, the rescale is
+      //    skipped.  P^T is packed to bf16 (nearest even) in the B-operand layout of PV.
       i16x4_t bp[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         float mx = fmaxf(fmaxf(sc[nt][0], sc[nt][1]), fmaxf(sc[nt][2], sc[nt][3]));
         mx = wave_max_xor_16_32(mx);
-        const float m_new = fmaxf(m_run[nt], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_new);
-        m_run[nt] = m_new;
+        if (mx > m_run[nt] + 8.f) {  // every tile holds a position below n, so mx is finite
+          const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - mx);
+          m_run[nt] = mx;
+          l_run[nt] *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+        }
+        const float m_ref = m_run[nt];
         uint32_t pk[2];
         float psum = 0.f;
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2) {
-          const uint32_t lo = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[nt][2 * i2] - m_new));
-          const uint32_t hi = float_to_bf16_bits(__builtin_amdgcn_exp2f(sc[nt][2 * i2 + 1] - m_new));
-          psum += bf16_bits_to_float(lo) + bf16_bits_to_float(hi);  // sum the weights actually used
-          pk[i2] = lo | (hi << 16);
+          pk[i2] = pack_bf16x2(__builtin_amdgcn_exp2f(sc[nt][2 * i2] - m_ref),
+                               __builtin_amdgcn_exp2f(sc[nt][2 * i2 + 1] - m_ref));
+          // sum the weights actually used
+          psum += __builtin_bit_cast(float, pk[i2] << 16) + __builtin_bit_cast(float, pk[i2] & 0xffff0000u);
         }
-        l_run[nt] = l_run[nt] * alpha + psum;
+        l_run[nt] += psum;
         bp[nt] = __builtin_bit_cast(i16x4_t, u32x2_t{pk[0], pk[1]});
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
       }
       // -- O^T += V^T P^T, V^T read transposed from LDS (rows 4q..4q+3 = tokens, column 16m + r)
 #pragma unroll

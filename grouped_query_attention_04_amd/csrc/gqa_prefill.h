@@ -40,9 +40,6 @@
 
 namespace gqa {
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 // Maximum over the four lanes l, l^16, l^32, l^48 (the four quads holding one matrix column).
 // v_permlane16_swap(x, x) hands back x of rows {0,0,2,2} and {1,1,3,3} (rows of 16 lanes), and
 // v_permlane32_swap(x, x) x of halves {0,0} and {1,1}: the larger of each pair pairs lane l with
@@ -56,11 +53,6 @@ __device__ __forceinline__ float quad_max_permlane(float x) {
   const uint32_t v = __builtin_bit_cast(uint32_t, x);
   const auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)c[0]), __builtin_bit_cast(float, (uint32_t)c[1]));
-}
-
-// Two floats to a bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 struct PrefillParams {
