@@ -3,6 +3,7 @@
 // gqa_prefill_api.hip and the planners in gqa_plan.cpp.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -27,8 +28,19 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int elt_bytes(int dt) { return dt == GQA_F32 ? 4 : dt == GQA_BF16 ? 2 : 1; }
 
+// The library's workgroup count.  Every segment that several workgroups share is merged at the end
+// by the one that finishes it last, in rounds of partial-result loads whose size grows with the
+// group; above 16 query heads per KV head a round takes four pieces.  With few (batch, KV head)
+// segments, 256 workgroups then cut each into 32 or more pieces whose merge outlasts the streaming
+// (B8 Hq32 Hkv1 L4096: 28.8 us at 256 workgroups, 19.9 us at 64), so there the count is capped at
+// eight pieces per segment on average, and at least 64 workgroups.
 int plan_workgroups(const gqa_shape_t* s) {
-  return s->num_workgroups > 0 ? s->num_workgroups : kDefaultWorkgroups;
+  if (s->num_workgroups > 0) return s->num_workgroups;
+  if (s->Hq / s->Hkv > 16) {
+    const long long cap = 8ll * s->B * s->Hkv;
+    return (int)std::max(64ll, std::min((long long)kDefaultWorkgroups, cap));
+  }
+  return kDefaultWorkgroups;
 }
 
 // Workspace: a counter area of fixed size (one counter per (batch, KV head), for up to kMaxUnits

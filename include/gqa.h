@@ -62,8 +62,10 @@ typedef struct {
   int32_t B, Hq, Hkv, L, d;
   int32_t q_dtype, kv_dtype, out_dtype; /* gqa_dtype_t values */
   float k_descale, v_descale;           /* 1.0 for f32 and bf16 caches */
-  int32_t num_workgroups; /* workgroups that split the cache: 0 = library's choice (256), else
-                             1..65536.  Results do not depend on it beyond rounding. */
+  int32_t num_workgroups; /* workgroups that split the cache: 0 = library's choice, else
+                             1..65536.  The choice is 256, except with more than 16 query heads
+                             per KV head: min(256, max(64, 8 * B * Hkv)).  Results do not depend
+                             on it beyond rounding. */
 } gqa_shape_t;
 
 /* Validates a shape (dimensions, divisibility, dtypes, workgroup count, 32-bit offsets).

@@ -86,6 +86,20 @@ def test_workspace_grows_with_workgroups_and_is_aligned():
     assert gqa.workspace_bytes(_shape(L=4096)) == gqa.workspace_bytes(_shape(L=4096, num_workgroups=256))
 
 
+def test_default_workgroup_count():
+    """256 workgroups, except for groups above 16 query heads: at most eight pieces per (batch, KV
+    head) segment on average, and at least 64 workgroups (the workspace holds two slots each)."""
+    def same(kw, wg):
+        return gqa.workspace_bytes(_shape(**kw)) == gqa.workspace_bytes(_shape(num_workgroups=wg, **kw))
+    bf = dict(q_dtype=gqa.BF16, kv_dtype=gqa.BF16, L=4096, d=128)
+    assert same(dict(B=8, Hq=32, Hkv=8, **bf), 256)
+    assert same(dict(B=8, Hq=16, Hkv=1, **bf), 256)      # G = 16: unchanged
+    assert same(dict(B=8, Hq=32, Hkv=1, **bf), 64)       # G = 32, 8 segments
+    assert same(dict(B=1, Hq=32, Hkv=1, **bf), 64)       # the floor
+    assert same(dict(B=20, Hq=64, Hkv=2, **bf), 256)     # 40 segments: 320 capped at 256
+    assert same(dict(B=12, Hq=32, Hkv=1, **bf), 96)
+
+
 def test_decode_rejects_before_any_hip_call():
     s = _shape()
     good = ctypes.c_void_p(1 << 20)   # never dereferenced: validation fails first
