@@ -281,24 +281,29 @@ prefill_mfma_kernel(PrefillParams p) {
     }
   };
   // -- O^T += V^T P^T and the row sums, for the block whose V is in LDS buffer vt: V^T rows 16m + r,
-  // keys 4q..4q+3 and 16+4q..16+4q+3 of each 32-key slab (two transposed reads)
-  auto pv = [&](const char* vt) __attribute__((always_inline)) {
+  // keys 4q..4q+3 and 16+4q..16+4q+3 of each 32-key slab (two transposed reads).  Each slab's eight
+  // fragments are read ahead of its products, so that the LDS latency is paid once per slab; the
+  // first slab's are read before the softmax, so that their latency hides behind the exponentials.
+  bf16x8_t av[MT];
+  auto read_v = [&](const char* vt, int sl) __attribute__((always_inline)) {
     const uint32_t vt_lds = (uint32_t)(uintptr_t)(GQA_LDS const char*)vt;
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl) {
-      bf16x8_t av[MT];  // read ahead of the products, so that the LDS latency is paid once per slab
+    for (int mt = 0; mt < MT; ++mt) {
+      i16x4_t part[2];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        i16x4_t part[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const uint32_t addr = vt_lds + (32 * sl + 16 * hf) * ROWB + voff[mt];
-          part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS i16x4_t*)(uintptr_t)addr);
-        }
-        av[mt] = __builtin_bit_cast(bf16x8_t, u32x4_t{
-            __builtin_bit_cast(u32x2_t, part[0])[0], __builtin_bit_cast(u32x2_t, part[0])[1],
-            __builtin_bit_cast(u32x2_t, part[1])[0], __builtin_bit_cast(u32x2_t, part[1])[1]});
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint32_t addr = vt_lds + (32 * sl + 16 * hf) * ROWB + voff[mt];
+        part[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS i16x4_t*)(uintptr_t)addr);
       }
+      av[mt] = __builtin_bit_cast(bf16x8_t, u32x4_t{
+          __builtin_bit_cast(u32x2_t, part[0])[0], __builtin_bit_cast(u32x2_t, part[0])[1],
+          __builtin_bit_cast(u32x2_t, part[1])[0], __builtin_bit_cast(u32x2_t, part[1])[1]});
+    }
+  };
+  auto pv = [&](const char* vt) __attribute__((always_inline)) {  // slab 0's fragments already in av
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      if (sl > 0) read_v(vt, sl);
       __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) lsum[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, bp[sl][nt], lsum[nt], 0, 0, 0);
@@ -320,6 +325,7 @@ prefill_mfma_kernel(PrefillParams p) {
     if (kb + 2 < nkb) load_block(kb + 2, par);
     if (!CAUSAL || kb * KB <= wave_hi) {
       qk(ks[P]);
+      read_v(vs[P], 0);
       softmax(kb);
       pv(vs[P]);
     }
