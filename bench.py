@@ -64,6 +64,18 @@ def recorded_traffic(wid, workgroups, paged=0):
     return float(val.group(1))
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (empty when unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(case, groups_b, paged=None):
     """Time the fp64 oracle (single thread) on every query head of batch entries [0, groups_b)."""
     from oracle import ref
@@ -84,7 +96,8 @@ def cpu_baseline(case, groups_b, paged=None):
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"all {case['Hq']} query heads of batch entries 0..{groups_b - 1} "
                       f"({groups_b * case['Hkv']} of {case['B'] * case['Hkv']} (batch, KV head) groups, "
-                      f"{kv_bytes / 1e6:.1f} MB of KV), single-threaded C, {dt:.1f} s"}
+                      f"{kv_bytes / 1e6:.1f} MB of KV), single-threaded C, {dt:.1f} s, on "
+                      f"{cpu_model() or 'an unnamed CPU'} ({os.cpu_count()} logical CPUs)"}
 
 
 def prefill_cpu_baseline(case, nrows=4000):
@@ -185,6 +198,8 @@ def main():
                     help="with --append: one launch stores the new rows and decodes (gqa_decode_append)")
     ap.add_argument("--paged", type=int, default=0, metavar="BS",
                     help="lay the cache out in pages of BS positions (0 = dense cache)")
+    ap.add_argument("--mean-lengths", action="store_true",
+                    help="give every sequence the workload's mean length (a stable trend line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-batches", type=int, default=32)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -211,6 +226,10 @@ def main():
     torch.cuda.set_device(dev)
     log(f"workload {wid}: {w.name}; generating inputs")
     case = workloads.make(wid)
+    if args.mean_lengths:
+        n = int(round(float(case["seq_lens"].double().mean())))
+        case["seq_lens"] = torch.full_like(case["seq_lens"], n)
+        log(f"every sequence set to the mean length {n}")
     elt = {"f32": 4, "bf16": 2, "fp8_e4m3": 1}[w.kv_dtype]
     sl = case["seq_lens"]
     kv_bytes = int(sl.sum()) * w.Hkv * 2 * w.d * elt
@@ -345,7 +364,7 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy of {args.calib_copy_mib} MiB done")
 
-    traffic = recorded_traffic(wid, args.workgroups, args.paged)
+    traffic = None if args.mean_lengths else recorded_traffic(wid, args.workgroups, args.paged)
     layout = f"paged, {args.paged} positions per page, random page placement" if paged else "dense"
     if args.append:
         layout += ("; each step appends the new token's K/V (bf16 rows) and decodes, in one launch" if args.fused
@@ -356,7 +375,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.kv_dtype, "data": "synthetic",
-        "config": {"workload": w.name + (f" paged bs{args.paged}" if paged else "") + (
+        "config": {"workload": w.name + (" mean lengths" if args.mean_lengths else "") + (f" paged bs{args.paged}" if paged else "") + (
                        (" fused append+decode" if args.fused else " append+decode") if args.append else ""),
                    "cache_layout": layout,
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d, "L": w.L,
