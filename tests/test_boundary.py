@@ -265,3 +265,22 @@ def test_fused_append_binding_validates_new_rows():
         gqa.decode_append_paged(q, kn, kn[:1], pages, pages, table, sl)
     with pytest.raises(ValueError):
         gqa.decode_append_paged(q, kn, kn, pages, pages, table, sl)   # CPU tensors are refused
+
+
+def test_header_is_c99_and_a_c_caller_links_and_runs(tmp_path):
+    """tests/c_abi/abi_check.c includes include/gqa.h as strict C99, links against the built library
+    and calls its host-side entry points (no GPU needed: every call returns before any HIP call)."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.dirname(gqa.LIB_PATH)
+    exe = str(tmp_path / "abi_check")
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-Wpedantic", "-Werror", "-I", os.path.join(root, "include"),
+           os.path.join(root, "tests", "c_abi", "abi_check.c"), "-o", exe, "-L", lib_dir, "-l:libgqa.so",
+           "-Wl,-rpath," + lib_dir, "-Wl,-rpath-link,/opt/rocm/lib", "-Wl,--allow-shlib-undefined"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
