@@ -187,7 +187,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4-mha, 4-gqa, 4-mqa, 5, 3-tp8)")
+    ap.add_argument("--workload", default="3", help="workload id (1, 2, 3, 4-mha, 4-gqa, 4-mqa, 5, 3-tp8, 3-d64)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated (0 = enough for 2 GiB)")
     ap.add_argument("--workgroups", type=int, default=0, help="workgroups (0 = library choice)")
     ap.add_argument("--prefill", default="", metavar="NAME",

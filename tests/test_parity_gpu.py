@@ -346,7 +346,7 @@ def _sample_rows(case, extra=16, seed=0):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, "4-mha", "4-gqa", "4-mqa", 5, "3-tp8"])
+@pytest.mark.parametrize("wid", [1, 2, 3, "4-mha", "4-gqa", "4-mqa", 5, "3-tp8", "3-d64"])
 def test_workload_parity(wid):
     """Each named workload at full size, in the launch configuration the benchmark times (library's
     workgroup count); the oracle checks every row of workload 1 and a sample of rows otherwise."""

@@ -69,6 +69,9 @@ WORKLOADS = {
     # its 8 query heads per GPU; same seed, so the same sequence lengths as the whole step
     "3-tp8": Workload("llama-70b-layer tp8-rank B32 Hq8 Hkv1 d128 L8192", 32, 8, 1, 128, 8192, "bf16", "bf16",
                       seq_range=(6000, 8192), seed=1003),
+    # the same step with head dim 64 (the other supported head size): half the bytes per token
+    "3-d64": Workload("llama-70b-layer head-dim-64 B32 Hq64 Hkv8 d64 L8192", 32, 64, 8, 64, 8192, "bf16", "bf16",
+                      seq_range=(6000, 8192), seed=1003),
 }
 
 
