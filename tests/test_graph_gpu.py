@@ -1,4 +1,5 @@
-"""The decode entry points under HIP graph capture (torch.cuda.CUDAGraph), through the C ABI.
+"""The decode entry points under HIP graph capture (torch.cuda.CUDAGraph) and on concurrent
+streams, through the C ABI.
 
 A serving loop captures its per-layer launches once and replays them.  The library only enqueues
 kernels on the caller's stream (no allocation, no memset, no synchronisation) and every call leaves
@@ -90,3 +91,26 @@ def test_captured_fused_append_paged_replays_bitwise():
         torch.cuda.synchronize()
         assert _bitwise(out, eager), f"replay {rep} differs from the eager result"
         assert _bitwise(kp, kp_e) and _bitwise(vp, vp_e), f"replay {rep} changed the pages differently"
+
+
+def test_two_streams_with_their_own_workspaces():
+    """Calls that overlap in time on two streams, each with its own workspace (the binding keeps
+    one per stream), both match the oracle; the library never synchronises."""
+    say("two streams")
+    cases = [workloads.make_case(8, 32, 8, 128, 2000, "bf16", "bf16", seq_range=(1, 2000), seed=130 + i)
+             for i in range(2)]
+    dev = [{n: c[n].to(DEV) for n in ("q", "k", "v", "seq_lens")} for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = [[], []]
+    for rep in range(3):
+        for i in (0, 1):
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(gqa.decode(dev[i]["q"], dev[i]["k"], dev[i]["v"], dev[i]["seq_lens"],
+                                          cases[i]["scale"], out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        want = ref.decode(cases[i]["q"], cases[i]["k"], cases[i]["v"], cases[i]["seq_lens"].numpy(),
+                          cases[i]["scale"], "bf16", "bf16")
+        compare(outs[i][0], want, "bf16", f"stream {i}")
+        assert all(_bitwise(o, outs[i][0]) for o in outs[i][1:]), f"stream {i}: repeated calls differ"
