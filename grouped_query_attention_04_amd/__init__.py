@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the decode runs in the HIP kernels of ``libgqa.so``; torch
 supplies device memory and the current stream.  The library must have been built
-(``python -m grouped_query_attention_04_amd.build``); importing this package without it raises.
+(``python grouped_query_attention_04_amd/build.py``); importing this package without it raises.
 
 ``decode`` computes, for each batch entry b and query head h with G = Hq // Hkv,
 ``out[b, h] = softmax(scale * q[b, h] . k_cache[b, h // G, :n]) @ v_cache[b, h // G, :n]`` with
@@ -72,7 +72,7 @@ EXPORTS = ["gqa_shape_check", "gqa_decode_workspace_bytes", "gqa_workspace_init"
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m grouped_query_attention_04_amd.build` (hipcc, gfx950)")
+                          "`python grouped_query_attention_04_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz, pS = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.POINTER(Shape)
     lib.gqa_shape_check.argtypes = [pS]

@@ -1,4 +1,7 @@
-"""Compile libgqa.so (HIP, gfx950) in-tree: ``python -m grouped_query_attention_04_amd.build``."""
+"""Compile libgqa.so (HIP, gfx950) in-tree: ``python grouped_query_attention_04_amd/build.py``.
+
+Run it as a script (or load it from its file): the package itself refuses to import until the library
+it binds exists."""
 import os
 import subprocess
 import sys
