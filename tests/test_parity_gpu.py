@@ -378,3 +378,36 @@ def test_nonpositive_scales(qd, kd, scale):
     say(f"decode scale {scale} q={qd} kv={kd}")
     case = workloads.make_case(3, 16, 4, 128, 900, qd, kd, seq_lens=(900, 517, 3), seed=14)
     compare(run(case, out_dtype="f32", scale=scale), oracle_full(case, scale=scale), kd, f"scale {scale}")
+
+
+# ------------------------------------------------------------------------------ seeded random shapes
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+        G = int(rng.integers(1, 33))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 7))
+        L = int(rng.integers(1, 1500))
+        sl = tuple(int(x) for x in rng.integers(0, L + 1, size=B))
+        kd = str(rng.choice(["bf16", "fp8_e4m3", "f32"]))
+        wg = int(rng.choice([0, 1, 3, 37, 256, 700]))
+        out.append((B, G * Hkv, Hkv, d, L, sl, kd, wg))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_shapes(24, 7), ids=lambda c: "B{}Hq{}Hkv{}d{}L{}-{}-wg{}".format(*c[:5], c[6], c[7]))
+def test_random_shapes(cfg):
+    """Seeded random shapes (any group size 1..32, odd KV head counts, empty and ragged sequences,
+    odd workgroup counts, every cache dtype) against the oracle."""
+    B, Hq, Hkv, d, L, sl, kd, wg = cfg
+    qd = "f32" if kd == "f32" else "bf16"
+    say(f"random shape {cfg}")
+    seed = (131 * B + 17 * Hq + 7 * Hkv + d + 3 * L + wg + sum(sl)) % 100000
+    case = workloads.make_case(B, Hq, Hkv, d, L, qd, kd, seq_lens=sl, seed=seed)
+    got = run(case, out_dtype="f32", workgroups=wg)
+    compare(got, oracle_full(case), kd, f"random {cfg}")
+    for b, n in enumerate(sl):
+        if n == 0:
+            assert (got[b] == 0).all()
