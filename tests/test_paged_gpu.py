@@ -132,3 +132,32 @@ def test_paged_negative_scale():
     case["scale"] = -0.2
     pg = workloads.paginate(case, 32, seed=16)
     compare(run_paged(case, pg), oracle_paged(case, pg), "bf16", "paged scale -0.2")
+
+
+def _random_paged(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.integers(1, 33))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 6))
+        bs = int(rng.choice([16, 32, 64, 128, 256, 512]))
+        L = int(rng.integers(1, 2000))
+        sl = tuple(int(x) for x in rng.integers(0, L + 1, size=B))
+        kd = str(rng.choice(["bf16", "fp8_e4m3"]))
+        wg = int(rng.choice([0, 1, 5, 256, 600]))
+        out.append((B, G * Hkv, Hkv, d, L, sl, bs, kd, wg))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_paged(16, 11),
+                         ids=lambda c: "B{}Hq{}Hkv{}d{}L{}".format(*c[:5]) + "-bs{}-{}-wg{}".format(*c[6:]))
+def test_paged_random_shapes(cfg):
+    """Seeded random paged shapes against the oracle (random page placement, spare pages)."""
+    B, Hq, Hkv, d, L, sl, bs, kd, wg = cfg
+    say(f"paged random shape {cfg}")
+    seed = (131 * B + 17 * Hq + 7 * Hkv + d + 3 * L + bs + wg + sum(sl)) % 100000
+    case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", kd, seq_lens=sl, seed=seed)
+    pg = workloads.paginate(case, bs, seed=seed + 1, spare_pages=3)
+    compare(run_paged(case, pg, out_dtype="f32", workgroups=wg), oracle_paged(case, pg), kd, f"paged random {cfg}")

@@ -105,3 +105,27 @@ def test_prefill_nonpositive_scales(scale, causal):
         mean = mean.repeat_interleave(G, dim=1)
         # the weights are exactly 1 (bf16), so only the fp32 accumulation order separates the two
         assert (got.cpu().double() - mean).abs().max() < 1e-5
+
+
+def _random_prefill(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 3))
+        S = int(rng.integers(1, 400))
+        causal = bool(rng.integers(0, 2))
+        out.append((B, G * Hkv, Hkv, S, d, causal))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_prefill(12, 13), ids=lambda c: "B{}Hq{}Hkv{}S{}d{}-causal{}".format(*c))
+def test_prefill_random_shapes(cfg):
+    """Seeded random prompt shapes (every supported group size, ragged query and key blocks)."""
+    B, Hq, Hkv, S, d, causal = cfg
+    say(f"prefill random shape {cfg}")
+    case = workloads.make_prefill_case(B, Hq, Hkv, d, S, seed=(131 * B + 17 * Hq + 7 * Hkv + 3 * S + d) % 100000)
+    want = ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", causal)
+    compare(run(case, causal, torch.float32), want, "bf16", f"prefill random {cfg}")
