@@ -49,6 +49,10 @@ def test_valid_shapes_pass():
     assert gqa.shape_check(_shape(d=128, q_dtype=gqa.BF16, kv_dtype=gqa.FP8_E4M3, out_dtype=gqa.F32)) == 0
     assert gqa.shape_check(_shape(Hq=32, Hkv=1, q_dtype=gqa.BF16, kv_dtype=gqa.BF16)) == 0
     assert gqa.shape_check(_shape(Hq=6, Hkv=2, num_workgroups=7)) == 0
+    # the largest per-head slice: L * d * bytes just under 2^31
+    for L, kv in [((1 << 23) - 1, gqa.BF16), ((1 << 24) - 1, gqa.FP8_E4M3)]:
+        assert gqa.shape_check(_shape(B=1, Hkv=1, L=L, d=128, q_dtype=gqa.BF16, kv_dtype=kv)) == 0
+        assert gqa.shape_check(_shape(B=1, Hkv=1, L=L + 1, d=128, q_dtype=gqa.BF16, kv_dtype=kv)) == 2
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -370,6 +370,28 @@ def test_workload_parity(wid):
     compare(sel, want, w.kv_dtype, f"workload {wid} {len(rows)} rows")
 
 
+def test_largest_segment_the_abi_takes():
+    """One (batch, KV head) segment at the largest size the C ABI accepts: L * d * 2 bytes just
+    under 2^31 (bf16, d = 128, L = 2^23 - 1 = 8,388,607 positions, so the last tile is ragged),
+    filled by one sequence.  The library's 256 workgroups each hold one piece of it, so the merge
+    combines 256 pieces.  One row against the oracle (it takes the oracle tens of seconds), and the
+    last row of the cache read through a needle at position L - 1."""
+    L = (1 << 23) - 1
+    assert gqa.shape_check(gqa.make_shape(1, 8, 1, L, 128, gqa.BF16, gqa.BF16)) == 0
+    say(f"largest segment: B1 Hq8 Hkv1 d128 L{L}")
+    case = workloads.make_case(1, 8, 1, 128, L, "bf16", "bf16", seq_lens=[L], seed=140)
+    got = run(case, out_dtype="f32").cpu()
+    want = ref.decode_rows(case["q"], case["k"], case["v"], case["seq_lens"].numpy(), case["scale"],
+                           [(0, 5)], "bf16", "bf16")
+    compare(got[0, 5:6], want, "bf16", "largest segment, head 5")
+    # needle: the key at the last position is q0 scaled so that its score beats every other by far
+    q0 = case["q"][0, 0].float()
+    case["k"][0, 0, L - 1] = (q0 * (400.0 / q0.dot(q0).item())).to(torch.bfloat16)
+    got = run(case, out_dtype="f32").cpu()
+    assert torch.allclose(got[0, 0].double(), case["v"][0, 0, L - 1].double(), atol=1e-3), \
+        "the needle at the last position was not found"
+
+
 @pytest.mark.parametrize("qd,kd", DTYPES)
 @pytest.mark.parametrize("scale", [-0.13, 0.0])
 def test_nonpositive_scales(qd, kd, scale):
