@@ -1,7 +1,8 @@
-"""Caches and page pools larger than 4 GiB, through the C ABI.
+"""Caches, page pools and prefill buffers larger than 4 GiB, through the C ABI.
 
 Byte offsets past 2^32 must survive every address computation: the segment bases of a dense cache,
-the page bases of a pool, and the rows the fused append writes.  The big buffers are built on the
+the page bases of a pool, the rows the fused append writes, and the query and output rows of the
+prefill.  The big buffers are built on the
 device and filled with NaN; the rows of a small seeded case are copied to their places far inside
 them (positions past each sequence's end stay NaN), so the oracle runs on the small case, and a read
 of a wrong row, or of a row never written, shows.
@@ -125,3 +126,32 @@ def test_paged_pool_beyond_4gib(kd):
         pages = pool.view(RAW[kd]).index_select(0, idx).cpu().numpy()
         expect = np.stack(exp)
         assert np.array_equal(pages, expect.view(pages.dtype)), "pages differ from the oracle's append"
+
+
+def test_prefill_buffers_beyond_4gib():
+    """Prefill with q and out of 4.6 GB each (B1100 Hq32 Hkv8 S512 d128): the first and the last
+    batch entries hold a seeded case (the last one starts past byte offset 2^32 of q and out), every
+    other entry is zero, whose output is exactly zero."""
+    Bb, Hq, Hkv, S, d = 1100, 32, 8, 512, 128
+    assert (Bb - 1) * Hq * S * d * 2 > (1 << 32)
+    say(f"prefill beyond 4 GiB: B{Bb} Hq{Hq} Hkv{Hkv} S{S} d{d}")
+    c = workloads.make_prefill_case(2, Hq, Hkv, d, S, seed=180)
+    q = torch.zeros(Bb, Hq, S, d, dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros(Bb, Hkv, S, d, dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros(Bb, Hkv, S, d, dtype=torch.bfloat16, device=DEV)
+    for src, dst in ((0, 0), (1, Bb - 1)):
+        q[dst] = c["q"][src].to(DEV)
+        k[dst] = c["k"][src].to(DEV)
+        v[dst] = c["v"][src].to(DEV)
+    out = gqa.prefill(q, k, v, c["scale"], causal=True)
+    torch.cuda.synchronize()
+    del q, k, v
+    rng = np.random.default_rng(181)
+    rows = sorted({(b, int(h), int(i)) for b in (0, 1) for h, i in
+                   zip(rng.integers(0, Hq, 24), rng.integers(0, S, 24))} |
+                  {(1, 0, 0), (1, Hq - 1, S - 1), (0, Hq - 1, S - 1)})
+    want = ref.prefill(c["q"], c["k"], c["v"], c["scale"], "bf16", True, rows=rows)
+    got = torch.stack([out[0 if b == 0 else Bb - 1, h, i] for b, h, i in rows])
+    compare(got, want, "bf16", f"prefill, {len(rows)} rows of the first and last entries")
+    for b in (1, Bb // 2, Bb - 2):
+        assert (out[b] == 0).all(), f"batch entry {b} (all zero inputs) is not zero"
