@@ -288,3 +288,22 @@ def test_header_is_c99_and_a_c_caller_links_and_runs(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_binding_refuses_to_import_without_the_library(tmp_path):
+    """No CPU fallback: a copy of the package without libgqa.so raises ImportError on import, naming
+    the build step."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "grouped_query_attention_04_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(gqa.__file__), "__init__.py"), pkg / "__init__.py")
+    code = ("import sys; sys.path.insert(0, sys.argv[1])\n"
+            "try:\n    import grouped_query_attention_04_amd\nexcept ImportError as e:\n"
+            "    print('ImportError:', e); sys.exit(3)\n"
+            "sys.exit(0)\n")
+    r = subprocess.run([sys.executable, "-c", code, str(tmp_path)], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 3, (r.returncode, r.stdout, r.stderr)
+    assert "libgqa.so is missing" in r.stdout and "build.py" in r.stdout
