@@ -3,9 +3,16 @@
 Inputs are passed as raw storage: float32 arrays for fp32, uint16 bit patterns for bf16 and uint8 codes
 for fp8-e4m3fn, together with a dtype name.  torch CPU tensors are accepted and reinterpreted as that
 raw storage without any arithmetic.  Results come back as float64 numpy arrays.
+
+``threads`` (decode_rows, decode_paged with rows, prefill with rows, and ``decode_all``): the listed
+rows are cut into contiguous chunks, one per thread, and each thread calls the same single-threaded
+C function on its chunk with its own scratch and output slice.  ctypes releases the GIL for the
+call, so the chunks run on separate cores.  Each row is computed by the same code either way, so
+the result is bitwise the single-threaded one.
 """
 import ctypes
 import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -88,6 +95,26 @@ def _args(q, k, v, seq_lens, scale, q_dtype, kv_dtype, k_descale, v_descale):
     return args, keep, (B, Hq, Hkv, L, d)
 
 
+def host_threads():
+    """CPUs this process may run on (the affinity mask, not the machine's count)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def _run_chunks(nrows, threads, call):
+    """call(lo, hi) for contiguous chunks of [0, nrows) on up to `threads` threads; returns the first
+    non-zero return code (or 0)."""
+    threads = max(1, min(int(threads), nrows))
+    if threads == 1:
+        return call(0, nrows)
+    bounds = [nrows * i // threads for i in range(threads + 1)]
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        rcs = list(ex.map(lambda i: call(bounds[i], bounds[i + 1]), range(threads)))
+    return next((rc for rc in rcs if rc), 0)
+
+
 def _raise(rc):
     if rc == 1:
         raise ValueError("oracle: invalid shape or dtype")
@@ -111,17 +138,32 @@ def decode(q, k, v, seq_lens, scale, q_dtype="f32", kv_dtype="f32", k_descale=1.
 
 
 def decode_rows(q, k, v, seq_lens, scale, rows, q_dtype="f32", kv_dtype="f32", k_descale=1.0,
-                v_descale=1.0):
+                v_descale=1.0, threads=1):
     """Only the listed (b, h) rows: returns [len(rows), d] float64."""
     args, keep, (B, Hq, Hkv, L, d) = _args(q, k, v, seq_lens, scale, q_dtype, kv_dtype, k_descale,
                                            v_descale)
     r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
     out = np.zeros((r.shape[0], d), dtype=np.float64)
-    w = np.zeros(max(L, 1), dtype=np.float64)
-    _raise(lib().gqa_oracle_decode_rows(*args, r.ctypes.data, r.shape[0], w.ctypes.data,
-                                        out.ctypes.data))
+
+    def chunk(lo, hi):
+        w = np.zeros(max(L, 1), dtype=np.float64)
+        return lib().gqa_oracle_decode_rows(*args, r[lo:hi].ctypes.data, hi - lo, w.ctypes.data,
+                                            out[lo:hi].ctypes.data)
+
+    _raise(_run_chunks(r.shape[0], threads, chunk))
     del keep
     return out
+
+
+def decode_all(q, k, v, seq_lens, scale, q_dtype="f32", kv_dtype="f32", k_descale=1.0, v_descale=1.0,
+               threads=None):
+    """Every (b, h) row, out[B, Hq, d] float64, on `threads` threads (default: every CPU this process
+    may use).  Bitwise equal to decode()."""
+    B, Hq = raw(q, q_dtype).shape[:2]
+    rows = [(b, h) for b in range(B) for h in range(Hq)]
+    out = decode_rows(q, k, v, seq_lens, scale, rows, q_dtype, kv_dtype, k_descale, v_descale,
+                      threads=host_threads() if threads is None else threads)
+    return out.reshape(B, Hq, -1)
 
 
 def weights(q, k, v, seq_lens, scale, b, h, q_dtype="f32", kv_dtype="f32", k_descale=1.0,
@@ -138,9 +180,11 @@ def weights(q, k, v, seq_lens, scale, b, h, q_dtype="f32", kv_dtype="f32", k_des
 
 
 def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, rows=None, q_dtype="bf16",
-                 kv_dtype="bf16", k_descale=1.0, v_descale=1.0):
+                 kv_dtype="bf16", k_descale=1.0, v_descale=1.0, threads=1):
     """Decode over a paged cache.  k_pages, v_pages: [num_blocks, Hkv, block_size, d]; block_table:
-    [B, max_blocks] int32.  Returns out[B, Hq, d] (rows None) or [len(rows), d], float64."""
+    [B, max_blocks] int32.  Returns out[B, Hq, d] (rows None) or [len(rows), d], float64.  With
+    rows == "all" every (b, h) row is computed through the row path (on `threads` threads) and
+    returned as [B, Hq, d]."""
     qa = raw(q, q_dtype)
     ka, va = raw(k_pages, kv_dtype), raw(v_pages, kv_dtype)
     if qa.ndim != 3 or ka.ndim != 4 or va.shape != ka.shape:
@@ -157,20 +201,26 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale, rows=None, q
     if sl.shape[0] != B:
         raise ValueError("seq_lens must have B entries")
     L = block_size * max_blocks
+    every = isinstance(rows, str) and rows == "all"
+    if every:
+        rows = [(b, h) for b in range(B) for h in range(Hq)]
     if rows is None:
         r, nrows, out = None, 0, np.zeros((B, Hq, d), dtype=np.float64)
     else:
         r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
         nrows, out = r.shape[0], np.zeros((r.shape[0], d), dtype=np.float64)
-    w = np.zeros(max(L, 1), dtype=np.float64)
-    rc = lib().gqa_oracle_decode_paged(
-        qa.ctypes.data, DTYPES[q_dtype], ka.ctypes.data, va.ctypes.data, DTYPES[kv_dtype],
-        float(k_descale), float(v_descale), bt.ctypes.data, sl.ctypes.data, float(scale), B, Hq, Hkv,
-        block_size, max_blocks, num_blocks, d, None if r is None else r.ctypes.data, nrows,
-        w.ctypes.data, out.ctypes.data)
-    _raise(rc)
+
+    def chunk(lo, hi):
+        w = np.zeros(max(L, 1), dtype=np.float64)
+        return lib().gqa_oracle_decode_paged(
+            qa.ctypes.data, DTYPES[q_dtype], ka.ctypes.data, va.ctypes.data, DTYPES[kv_dtype],
+            float(k_descale), float(v_descale), bt.ctypes.data, sl.ctypes.data, float(scale), B, Hq, Hkv,
+            block_size, max_blocks, num_blocks, d, None if r is None else r[lo:hi].ctypes.data, hi - lo,
+            w.ctypes.data, out[lo:hi].ctypes.data if r is not None else out.ctypes.data)
+
+    _raise(chunk(0, 0) if r is None else _run_chunks(nrows, threads, chunk))
     del qa, ka, va, bt, sl
-    return out
+    return out.reshape(B, Hq, d) if every else out
 
 
 def kv_bytes_per_token(layers, kv_heads, head_dim, dtype_bytes=2):
@@ -222,9 +272,10 @@ def append(k_new, v_new, new_dtype, k_cache, v_cache, kv_dtype, positions, k_des
     return kc, vc, rc
 
 
-def prefill(q, k, v, scale, dtype="bf16", causal=True, rows=None):
+def prefill(q, k, v, scale, dtype="bf16", causal=True, rows=None, threads=1):
     """Prefill attention: q [B,Hq,S,d], k, v [B,Hkv,S,d] (raw storage of dtype).  Returns out
-    [B,Hq,S,d] (rows None) or [len(rows), d] for the listed (b, h, i) triples, float64."""
+    [B,Hq,S,d] (rows None) or [len(rows), d] for the listed (b, h, i) triples, float64; rows "all"
+    computes every row through the row path (on `threads` threads) and returns [B,Hq,S,d]."""
     qa, ka, va = raw(q, dtype), raw(k, dtype), raw(v, dtype)
     if qa.ndim != 4 or ka.ndim != 4 or va.shape != ka.shape:
         raise ValueError("q must be [B,Hq,S,d]; k and v [B,Hkv,S,d]")
@@ -232,15 +283,23 @@ def prefill(q, k, v, scale, dtype="bf16", causal=True, rows=None):
     Bk, Hkv, Sk, dk = ka.shape
     if (Bk, Sk, dk) != (B, S, d):
         raise ValueError("q and k/v disagree on B, S or d")
+    every = isinstance(rows, str) and rows == "all"
+    if every:
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(S), indexing="ij")
+        rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
     if rows is None:
         r, nrows, out = None, 0, np.zeros((B, Hq, S, d), dtype=np.float64)
     else:
         r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
         nrows, out = r.shape[0], np.zeros((r.shape[0], d), dtype=np.float64)
-    w = np.zeros(max(S, 1), dtype=np.float64)
-    rc = lib().gqa_oracle_prefill(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, DTYPES[dtype], float(scale),
-                                  1 if causal else 0, B, Hq, Hkv, S, d, None if r is None else r.ctypes.data,
-                                  nrows, w.ctypes.data, out.ctypes.data)
-    _raise(rc)
+
+    def chunk(lo, hi):
+        w = np.zeros(max(S, 1), dtype=np.float64)
+        return lib().gqa_oracle_prefill(qa.ctypes.data, ka.ctypes.data, va.ctypes.data, DTYPES[dtype],
+                                        float(scale), 1 if causal else 0, B, Hq, Hkv, S, d,
+                                        None if r is None else r[lo:hi].ctypes.data, hi - lo, w.ctypes.data,
+                                        out[lo:hi].ctypes.data if r is not None else out.ctypes.data)
+
+    _raise(chunk(0, 0) if r is None else _run_chunks(nrows, threads, chunk))
     del qa, ka, va
-    return out
+    return out.reshape(B, Hq, S, d) if every else out

@@ -15,7 +15,7 @@ import torch
 import grouped_query_attention_04_amd as gqa
 import workloads
 from oracle import ref
-from tests.test_parity_gpu import ABS_GATE, DEV, _sample_rows, compare, say
+from tests.test_parity_gpu import DEV, compare, rows_off, say
 
 pytestmark = pytest.mark.gpu
 
@@ -164,15 +164,19 @@ def test_fused_is_bitwise_the_two_calls(kv, paged_bs, wg):
     assert _bitwise(o1, o2), "outputs differ"
 
 
-@pytest.mark.parametrize("paged_bs", [None, 16])
-def test_fused_full_size_70b_layer(paged_bs):
-    """The 70B-layer decode step at full size (B32 Hq64 Hkv8 d128 L8192), library's workgroup
-    count: sampled output rows against the oracle's append + decode, the whole cache bit-exact
-    against the oracle's append, and everything bitwise against the two separate calls."""
-    w = workloads.WORKLOADS[3]
+FUSED_FULL = [(3, None), (3, 16), (2, None), (2, 32), ("4-gqa", 64), (5, None), (5, 64)]
+
+
+@pytest.mark.parametrize("wid,paged_bs", FUSED_FULL, ids=lambda x: str(x))
+def test_fused_full_size(wid, paged_bs):
+    """Named workloads at full size (the 70B layer, the 8B layer, the group-size sweep's GQA-8 point
+    and the long fp8 cache), library's workgroup count: every output row against the oracle's
+    append + decode, the whole cache bit-exact against the oracle's append, and everything bitwise
+    against the two separate calls."""
+    w = workloads.WORKLOADS[wid]
     say(f"fused full size: {w.name}, block_size {paged_bs}")
-    c = workloads.make(3)
-    B, Hkv, d = w.B, w.Hkv, w.d
+    c = workloads.make(wid)
+    B, Hkv, d, kv = w.B, w.Hkv, w.d, w.kv_dtype
     kn, vn = _new_rows(B, Hkv, d, 97)
     sl = c["seq_lens"]
     if paged_bs is not None:
@@ -182,20 +186,53 @@ def test_fused_full_size_70b_layer(paged_bs):
     assert _bitwise(o1, o2), "outputs differ"
     pos = (sl - 1).numpy()
     if paged_bs is None:
-        wk, wv, wskip = ref.append(kn, vn, "bf16", c["k"], c["v"], "bf16", pos)
+        wk, wv, wskip = ref.append(kn, vn, "bf16", c["k"], c["v"], kv, pos)
     else:
-        wk, wv, wskip = ref.append(kn, vn, "bf16", c["k_pages"], c["v_pages"], "bf16", pos,
+        wk, wv, wskip = ref.append(kn, vn, "bf16", c["k_pages"], c["v_pages"], kv, pos,
                                    block_table=c["block_table"].numpy())
     assert wskip == 0
-    assert np.array_equal(_raw(k2, "bf16"), wk.view(np.int16))
-    assert np.array_equal(_raw(v2, "bf16"), wv.view(np.int16))
+    assert np.array_equal(_raw(k2, kv), wk.view(_raw(k2, kv).dtype)), "K cache differs from the oracle's append"
+    assert np.array_equal(_raw(v2, kv), wv.view(_raw(v2, kv).dtype)), "V cache differs from the oracle's append"
     del k1, v1, k2, v2
-    rows = _sample_rows(c)
     if paged_bs is None:
-        want = ref.decode_rows(c["q"], wk, wv, sl.numpy(), c["scale"], rows, "bf16", "bf16")
+        want = ref.decode_all(c["q"], wk, wv, sl.numpy(), c["scale"], "bf16", kv)
     else:
-        want = ref.decode_paged(c["q"], wk, wv, c["block_table"].numpy(), sl.numpy(), c["scale"], rows,
-                                "bf16", "bf16")
-    sel = torch.stack([o2[b, h] for b, h in rows])
-    assert all(np.abs(sel[i].double().numpy() - want[i]).max() <= ABS_GATE["bf16"] for i in range(len(rows)))
-    compare(sel, want, "bf16", f"fused full size, {len(rows)} rows")
+        want = ref.decode_paged(c["q"], wk, wv, c["block_table"].numpy(), sl.numpy(), c["scale"], "all",
+                                "bf16", kv, threads=ref.host_threads())
+    bad = rows_off(o2, want, kv)
+    if bad:
+        say(f"  rows off the oracle: {bad[:20]}")
+    compare(o2, want, kv, f"fused full size, all {w.B * w.Hq} rows")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("paged_bs", [None, 32])
+@pytest.mark.parametrize("B,wg", [(300, 37), (1000, 0)], ids=lambda x: str(x))
+def test_fused_batches_above_256(B, wg, paged_bs, kv):
+    """The fused append + decode with more sequences than 256 and than workgroups: the whole cache
+    bit-exact against the oracle's append, every output row against the oracle's decode."""
+    from tests.test_parity_gpu import _serving_lengths
+
+    L = 300
+    sl = torch.tensor(_serving_lengths(B, L, seed=5 * B + wg), dtype=torch.int32)
+    say(f"fused batch {B}, {wg} workgroups, kv={kv}, block_size {paged_bs}")
+    c = workloads.make_case(B, 16, 2, 128, L, "bf16", kv, seq_lens=sl.tolist(), seed=B * 3 + wg)
+    kn, vn = _new_rows(B, 2, 128, 98)
+    if paged_bs is not None:
+        c = workloads.paginate(c, paged_bs, seed=17, spare_pages=3)
+    (o1, k1, v1), (o2, k2, v2) = _separate_and_fused(c, kn, vn, sl, 1.0, 1.0, wg, paged_bs)
+    assert _bitwise(k1, k2) and _bitwise(v1, v2), "caches differ"
+    assert _bitwise(o1, o2), "outputs differ"
+    pos = (sl - 1).numpy()
+    if paged_bs is None:
+        wk, wv, wskip = ref.append(kn, vn, "bf16", c["k"], c["v"], kv, pos)
+        want = ref.decode_all(c["q"], wk, wv, sl.numpy(), c["scale"], "bf16", kv)
+    else:
+        wk, wv, wskip = ref.append(kn, vn, "bf16", c["k_pages"], c["v_pages"], kv, pos,
+                                   block_table=c["block_table"].numpy())
+        want = ref.decode_paged(c["q"], wk, wv, c["block_table"].numpy(), sl.numpy(), c["scale"], "all",
+                                "bf16", kv, threads=ref.host_threads())
+    assert wskip == 0
+    assert np.array_equal(_raw(k2, kv), wk.view(_raw(k2, kv).dtype)), "K cache differs from the oracle's append"
+    assert np.array_equal(_raw(v2, kv), wv.view(_raw(v2, kv).dtype)), "V cache differs from the oracle's append"
+    compare(o2, want, kv, f"fused B{B} wg{wg}")

@@ -11,7 +11,7 @@ import torch
 import grouped_query_attention_04_amd as gqa
 import workloads
 from oracle import ref
-from tests.test_parity_gpu import ABS_GATE, DEV, TORCH, _sample_rows, compare, say
+from tests.test_parity_gpu import DEV, TORCH, compare, rows_off, say
 
 pytestmark = pytest.mark.gpu
 
@@ -29,11 +29,13 @@ def run_paged(case, pg, out_dtype=None, workgroups=0, table=None):
     return out
 
 
-def oracle_paged(case, pg, rows=None, table=None):
+def oracle_paged(case, pg, table=None):
+    """Every (b, h) row of the oracle over the pages, on all CPUs this process may use."""
     return ref.decode_paged(case["q"], pg["k_pages"], pg["v_pages"],
                             (pg["block_table"] if table is None else table).numpy(),
-                            case["seq_lens"].numpy(), case["scale"], rows, case["q_dtype"],
-                            case["kv_dtype"], case["k_descale"], case["v_descale"])
+                            case["seq_lens"].numpy(), case["scale"], "all", case["q_dtype"],
+                            case["kv_dtype"], case["k_descale"], case["v_descale"],
+                            threads=ref.host_threads())
 
 
 PAGED_SMALL = [
@@ -110,20 +112,18 @@ def test_paged_out_of_pool_entry_reads_zeros():
 
 @pytest.mark.parametrize("wid,bs", [(3, 16), (5, 64), (2, 32)])
 def test_paged_workload_parity(wid, bs):
-    """Full-size workloads in paged form, library's workgroup count, sampled rows vs the oracle."""
+    """Full-size workloads in paged form, library's workgroup count, every output row against the
+    oracle."""
     w = workloads.WORKLOADS[wid]
     say(f"paged workload {wid} block_size {bs}: {w.name}")
     case = workloads.make(wid)
     pg = workloads.paginate(case, bs, seed=9, spare_pages=8)
     got = run_paged(case, pg).cpu()
-    rows = _sample_rows(case)
-    want = oracle_paged(case, pg, rows=rows)
-    sel = torch.stack([got[b, h] for b, h in rows])
-    bad = [rows[i] for i in range(len(rows))
-           if not np.abs(sel[i].double().numpy() - want[i]).max() <= ABS_GATE[w.kv_dtype]]
+    want = oracle_paged(case, pg)
+    bad = rows_off(got, want, w.kv_dtype)
     if bad:
-        say(f"  rows off the oracle: {bad}")
-    compare(sel, want, w.kv_dtype, f"paged workload {wid} {len(rows)} rows")
+        say(f"  rows off the oracle: {bad[:20]}")
+    compare(got, want, w.kv_dtype, f"paged workload {wid} all {w.B * w.Hq} rows")
 
 
 def test_paged_negative_scale():
@@ -161,3 +161,22 @@ def test_paged_random_shapes(cfg):
     case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", kd, seq_lens=sl, seed=seed)
     pg = workloads.paginate(case, bs, seed=seed + 1, spare_pages=3)
     compare(run_paged(case, pg, out_dtype="f32", workgroups=wg), oracle_paged(case, pg), kd, f"paged random {cfg}")
+
+
+@pytest.mark.parametrize("kd", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("B,wg", [(300, 0), (1000, 37), (1000, 4096)], ids=lambda x: str(x))
+def test_paged_batches_above_256(B, wg, kd):
+    """Paged decode with more sequences than the one-pass range search takes (256) and than
+    workgroups: every row against the oracle."""
+    from tests.test_parity_gpu import _serving_lengths
+
+    L = 300
+    sl = _serving_lengths(B, L, seed=3 * B + wg)
+    say(f"paged batch {B}, {wg} workgroups, kv={kd}")
+    case = workloads.make_case(B, 16, 2, 128, L, "bf16", kd, seq_lens=sl, seed=B * 5 + wg)
+    pg = workloads.paginate(case, 32, seed=B, spare_pages=5)
+    got = run_paged(case, pg, out_dtype="f32", workgroups=wg)
+    compare(got, oracle_paged(case, pg), kd, f"paged B{B} wg{wg}")
+    for b, n in enumerate(sl):
+        if n == 0:
+            assert (got[b] == 0).all(), b
