@@ -188,10 +188,40 @@ def _stream_handle(device):
 _workspaces = {}
 
 
+def init_workspace(ws: torch.Tensor, shape) -> torch.Tensor:
+    """Initialises a workspace tensor (uint8, on the device) with gqa_workspace_init on torch's
+    current stream: the counter area cleared and the header tag written.  Returns ws."""
+    with torch.cuda.device(ws.device):
+        if isinstance(shape, PagedShape):
+            rc = lib.gqa_paged_workspace_init(ws.data_ptr(), ws.numel(), ctypes.byref(shape),
+                                              _stream_handle(ws.device))
+        else:
+            rc = lib.gqa_workspace_init(ws.data_ptr(), ws.numel(), ctypes.byref(shape),
+                                        _stream_handle(ws.device))
+    _check(rc)
+    return ws
+
+
+def new_workspace(shape, device, nbytes=None) -> torch.Tensor:
+    """A fresh workspace of max(nbytes, the shape's requirement) bytes, initialised."""
+    need = workspace_bytes(shape)
+    if need == 0:
+        _check(shape_check(shape))
+    ws = torch.empty(max(need, nbytes or 0, 256), dtype=torch.uint8, device=device)
+    return init_workspace(ws, shape)
+
+
+def workspace_errors(ws: torch.Tensor) -> int:
+    """Workgroups that refused this workspace for a missing header tag since its initialisation
+    (header word 2; reading it synchronises with the device)."""
+    return int(ws[8:12].view(torch.int32).item())
+
+
 def workspace_for(shape, device) -> torch.Tensor:
-    """A workspace cached per (device, stream), zeroed when allocated and grown when a shape needs
-    more.  The library leaves its counters at zero after every call, so one buffer serves every
-    shape.  Calls that overlap in time on different streams get different buffers."""
+    """A workspace cached per (device, stream), initialised when allocated and replaced by a larger
+    one when a shape needs more.  The library leaves its counters at zero after every call, so one
+    buffer serves every shape.  Calls that overlap in time on different streams get different
+    buffers."""
     need = workspace_bytes(shape)
     if need == 0:
         _check(shape_check(shape))
@@ -199,7 +229,7 @@ def workspace_for(shape, device) -> torch.Tensor:
     key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+        ws = new_workspace(shape, dev)
         _workspaces[key] = ws
     return ws
 

@@ -43,11 +43,13 @@ int plan_workgroups(const gqa_shape_t* s) {
   return kDefaultWorkgroups;
 }
 
-// Workspace: a counter area of fixed size (one counter per (batch, KV head), for up to kMaxUnits
-// of them), then two published-piece slots per workgroup.  Because the counter area never moves,
-// no shape's partial results ever land on another shape's counters, and since every call leaves its
-// counters at zero, a workspace zeroed once can serve calls of any shape.
+// Workspace: a 256-byte header (the initialisation tag and an error count), a counter area of
+// fixed size (one counter per (batch, KV head), for up to kMaxUnits of them), then two
+// published-piece slots per workgroup.  Because the counter area never moves, no shape's partial
+// results ever land on another shape's counters, and since every call leaves its counters at zero,
+// a workspace initialised once can serve calls of any shape.
 constexpr size_t kMaxUnits = size_t(1) << 18;
+constexpr size_t kHeaderBytes = gqa::kWorkspaceHeaderWords * sizeof(uint32_t);
 
 struct Layout {
   int workgroups;
@@ -59,8 +61,8 @@ Layout plan(const gqa_shape_t* s) {
   lo.workgroups = plan_workgroups(s);
   const size_t slots = (size_t)lo.workgroups * 2;  // two per workgroup
   const size_t G = (size_t)(s->Hq / s->Hkv);
-  lo.counters_off = 0;
-  lo.ml_off = kMaxUnits * sizeof(uint32_t);
+  lo.counters_off = kHeaderBytes;
+  lo.ml_off = kHeaderBytes + kMaxUnits * sizeof(uint32_t);
   lo.o_off = lo.ml_off + align_up(slots * G * 2 * sizeof(float));
   lo.total = lo.o_off + align_up(slots * G * (size_t)s->d * sizeof(float));
   return lo;
@@ -123,6 +125,7 @@ gqa::Params base_params(const void* q, const void* k, const void* v, const int32
   prm.out = out;
   char* ws = static_cast<char*>(workspace);
   prm.counters = reinterpret_cast<uint32_t*>(ws + lo.counters_off);
+  prm.header = reinterpret_cast<uint32_t*>(ws);
   prm.part_ml = reinterpret_cast<float*>(ws + lo.ml_off);
   prm.part_o = reinterpret_cast<float*>(ws + lo.o_off);
   prm.B = s->B;
@@ -221,8 +224,9 @@ gqa_status_t gqa_workspace_init(void* workspace, size_t workspace_bytes, const g
   if (!workspace || !aligned(workspace, 16)) return GQA_ERR_INVALID_ARG;
   const Layout lo = plan(s);
   if (workspace_bytes < lo.total) return GQA_ERR_WORKSPACE;
-  const int n = s->B * s->Hkv;
-  hipLaunchKernelGGL(gqa::clear_u32_kernel, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream,
+  // the header and the whole counter area, whatever this shape's count of (batch, KV head) units
+  const int n = (int)((kHeaderBytes + kMaxUnits * sizeof(uint32_t)) / sizeof(uint32_t));
+  hipLaunchKernelGGL(gqa::init_workspace_kernel, dim3((n + 255) / 256), dim3(256), 0, (hipStream_t)stream,
                      static_cast<uint32_t*>(workspace), n);
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }

@@ -34,6 +34,7 @@ struct Params {
   float* part_o;       // [W][2][G][D] unnormalised outputs of published pieces
   float* part_ml;      // [W][2][G][2] their (max, sum), base-2 domain
   uint32_t* counters;  // [B*Hkv] finished-piece counters, zero between calls
+  uint32_t* header;    // workspace header: tag words 0-1, error count word 2
   int B, Hq, Hkv, L, G;
   int W;            // workgroups launched
   float qk_scale;   // scale * k_descale * log2(e)
@@ -49,6 +50,35 @@ struct Params {
   int32_t* skipped;  // optional: sequences whose new position lies past the cache or on a page outside the pool
   float k_enc_descale, v_enc_descale;
 };
+
+// ------------------------------------------------------------------------------------------------
+// Workspace header.  gqa_workspace_init clears the counter area and then writes this two-word tag at
+// the start of the workspace.  The merge of shared segments relies on counters that start at zero; a
+// workspace without the tag (never initialised, or overwritten) is refused by every workgroup, which
+// fills its output rows with NaN and counts itself in header word 2 instead of touching a counter.
+constexpr uint32_t kWorkspaceTag0 = 0x41514721u, kWorkspaceTag1 = 0x5EED0C7Au;
+constexpr int kWorkspaceHeaderWords = 64;  // 256 bytes before the counter area
+
+// Both tag words, read with scalar loads; the caller compares them later, so the load's latency
+// overlaps with whatever comes in between.
+__device__ __forceinline__ u32x2_t workspace_tag(const Params& p) {
+  const GQA_CONST u32x2_t* h = (const GQA_CONST u32x2_t*)(uintptr_t)p.header;
+  return *h;
+}
+
+__device__ __forceinline__ bool workspace_ok(u32x2_t tag) {
+  return tag[0] == kWorkspaceTag0 && tag[1] == kWorkspaceTag1;
+}
+
+// The refusal: NaN in the output rows of batch entries b = blockIdx.x + k * W, and one count.
+template <int D, typename OutT, int NTH>
+__device__ void refuse_workspace(const Params& p) {
+  for (int b = blockIdx.x; b < p.B; b += p.W) {
+    OutT* out = reinterpret_cast<OutT*>(p.out) + (size_t)b * p.Hq * D;
+    for (int i = threadIdx.x; i < p.Hq * D; i += NTH) store_out(out + i, __builtin_nanf(""));
+  }
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(p.header + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ------------------------------------------------------------------------------------------------
 // Tile space and its split over workgroups.
@@ -417,6 +447,13 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
   // fused append: per wave, the new K and V rows in the cache format (unused otherwise)
   __shared__ __attribute__((aligned(16))) char ascr[APPEND ? NW * 2 * ROWB : 16];
 
+  const u32x2_t tag = workspace_tag(p);
+  Range rg;
+  const bool busy = find_range<TILE, NTH>(p, sh, rg);
+  if (!workspace_ok(tag)) {
+    refuse_workspace<D, OutT, NTH>(p);
+    return;
+  }
   if constexpr (APPEND) {
     // sequences whose new position lies past the cache: counted once, by workgroup b mod W
     if (p.skipped && threadIdx.x == 0)
@@ -424,8 +461,7 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
         if (p.seq_lens[b] > p.L) __hip_atomic_fetch_add(p.skipped, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   zero_empty_rows<D, OutT, NTH>(p);
-  Range rg;
-  if (!find_range<TILE, NTH>(p, sh, rg)) return;
+  if (!busy) return;
 
   const int w = uniform((int)threadIdx.x / 64);  // wave index, scalar: tile addressing derives from it
   const int l = threadIdx.x % 64;
@@ -746,9 +782,15 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ Shared sh;
 
-  zero_empty_rows<D, OutT, NTH>(p);
+  const u32x2_t tag = workspace_tag(p);
   Range rg;
-  if (!find_range<TILE, NTH>(p, sh, rg)) return;
+  const bool busy = find_range<TILE, NTH>(p, sh, rg);
+  if (!workspace_ok(tag)) {
+    refuse_workspace<D, OutT, NTH>(p);
+    return;
+  }
+  zero_empty_rows<D, OutT, NTH>(p);
+  if (!busy) return;
   const int w = threadIdx.x / 64;
   const int l = threadIdx.x % 64;
   const int G = p.G;
@@ -843,10 +885,11 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
 }
 
 // ------------------------------------------------------------------------------------------------
-// Workspace counter clear (a kernel rather than a memset so that it may be captured in a graph).
-__global__ void clear_u32_kernel(uint32_t* p, int n) {
+// Workspace initialisation: the header and the whole counter area cleared, then the tag written (a
+// kernel rather than a memset so that it may be captured in a graph).  n = words to clear.
+__global__ void init_workspace_kernel(uint32_t* ws, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+  if (i < n) ws[i] = i == 0 ? kWorkspaceTag0 : i == 1 ? kWorkspaceTag1 : 0u;
 }
 
 // seq_lens range check (test helper).

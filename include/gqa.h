@@ -72,16 +72,26 @@ typedef struct {
  * Host only; no HIP call.  Returns GQA_OK, GQA_ERR_INVALID_ARG or GQA_ERR_UNSUPPORTED. */
 gqa_status_t gqa_shape_check(const gqa_shape_t* shape);
 
-/* Bytes of device workspace gqa_decode needs for this shape: a fixed 1 MiB area of counters (one
- * per (batch, KV head); B * Hkv may not exceed 2^18) followed by two partial-result slots per
- * workgroup.  0 if the shape is invalid.  Host only. */
+/* Bytes of device workspace gqa_decode needs for this shape: a 256-byte header, a fixed 1 MiB area
+ * of counters (one per (batch, KV head); B * Hkv may not exceed 2^18), then two partial-result slots
+ * per workgroup.  0 if the shape is invalid.  Host only.
+ *
+ * Header: bytes 0-7 hold a tag that only gqa_workspace_init writes; bytes 8-11 are a uint32 error
+ * count.  The merge of a (batch, KV head) segment that several workgroups share is done by the one
+ * that finishes last, found with the segment's counter, so the counters must start at zero. */
 size_t gqa_decode_workspace_bytes(const gqa_shape_t* shape);
 
-/* Clears the counter area of a workspace.  A workspace must be cleared once (by this call or by
- * zero-filling it) before its first gqa_decode; every gqa_decode that completes leaves the counters
- * at zero again, so the workspace then serves later calls of any shape that fits in it.  Writing
- * anything else into the counter area requires clearing it again.  Enqueues one small kernel on
- * `stream` (a hipStream_t, NULL = the default stream). */
+/* Initialises a workspace: clears the error count and the whole counter area (every counter, not
+ * only this shape's) and writes the tag.  Required once before the first decode on a workspace;
+ * every decode that completes leaves the counters at zero again, so the workspace then serves later
+ * calls of any shape that fits in it, on one stream at a time.  Zero-filling is not initialisation.
+ * A decode, paged decode or fused append-decode given a workspace without the tag (for instance
+ * fresh memory from hipMalloc) does no work: every output row becomes NaN, no counter and no cache
+ * row is written, and each of its workgroups adds one to the header's error count.  The check does
+ * not see a counter area overwritten after initialisation (the result is then undefined);
+ * initialise again after writing into the workspace.  Enqueues one small kernel on `stream` (a
+ * hipStream_t, NULL = the default stream); returns GQA_ERR_WORKSPACE if workspace_bytes is below
+ * this shape's requirement. */
 gqa_status_t gqa_workspace_init(void* workspace, size_t workspace_bytes, const gqa_shape_t* shape,
                                 void* stream);
 

@@ -23,7 +23,7 @@ def _bitwise(a, b):
 
 
 def _ws(shape):
-    return torch.zeros(max(gqa.workspace_bytes(shape), 256), dtype=torch.uint8, device=DEV)
+    return gqa.new_workspace(shape, DEV)
 
 
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])

@@ -271,25 +271,88 @@ def test_output_guards_and_workspace_counters():
     buf = torch.full((n + 2 * 4096,), -7.0, dtype=torch.float32, device=DEV)
     out = buf[4096:4096 + n].view(2, 16, 128)
     shape = gqa.make_shape(2, 16, 4, 1200, 128, gqa.BF16, gqa.BF16, gqa.F32, num_workgroups=13)
-    ws = torch.zeros(gqa.workspace_bytes(shape) + 8192, dtype=torch.uint8, device=DEV)
-    ws[-8192:] = 0xA5
+    need = gqa.workspace_bytes(shape)
+    ws = gqa.new_workspace(shape, DEV, need + 8192)
+    ws[need:] = 0xA5
     gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"], case["scale"], out=out, num_workgroups=13,
                workspace=ws)
     torch.cuda.synchronize()
     assert (buf[:4096] == -7.0).all() and (buf[4096 + n:] == -7.0).all()
-    assert (ws[-8192:] == 0xA5).all()
-    assert (ws[: 1 << 20] == 0).all()        # the counter area is back at zero
+    assert (ws[need:] == 0xA5).all()
+    assert (ws[8:COUNTERS_END] == 0).all()        # error count and counter area back at zero
     compare(out, oracle_full(case), "bf16", "guarded")
 
 
-def test_workspace_init_clears_counters():
+# the workspace header (256 bytes: tag, error count) and the counter area (2^18 u32)
+COUNTERS_END = 256 + (1 << 20)
+
+
+def test_workspace_init_clears_the_whole_counter_area():
+    """gqa_workspace_init with a small shape clears the header and every counter (not only that
+    shape's), so a later call with many more (batch, KV head) units finds zeros."""
     say("workspace init")
-    shape = gqa.make_shape(2, 16, 4, 1200, 128, gqa.BF16, gqa.BF16, num_workgroups=13)
-    ws = torch.full((gqa.workspace_bytes(shape),), 0x11, dtype=torch.uint8, device=DEV)
     import ctypes
-    assert gqa.lib.gqa_workspace_init(ws.data_ptr(), ws.numel(), ctypes.byref(shape), None) == 0
+    small = gqa.make_shape(2, 16, 4, 1200, 128, gqa.BF16, gqa.BF16, num_workgroups=13)
+    big = workloads.make_case(96, 16, 8, 128, 300, "bf16", "bf16", seq_range=(0, 300), seed=42)
+    big_shape = gqa.make_shape(96, 16, 8, 300, 128, gqa.BF16, gqa.BF16, gqa.F32, num_workgroups=37)
+    ws = torch.full((gqa.workspace_bytes(big_shape),), 0x11, dtype=torch.uint8, device=DEV)
+    assert gqa.lib.gqa_workspace_init(ws.data_ptr(), ws.numel(), ctypes.byref(small), None) == 0
     torch.cuda.synchronize()
-    assert (ws[:32] == 0).all() and (ws[1 << 20:(1 << 20) + 256] == 0x11).all()
+    assert (ws[:8] != 0).any()                        # the tag
+    assert (ws[8:COUNTERS_END] == 0).all()            # error count and all 2^18 counters
+    assert (ws[COUNTERS_END:] == 0x11).all()          # partial slots untouched
+    d = to_dev(big)
+    out = gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"], big["scale"], out_dtype=torch.float32,
+                     num_workgroups=37, workspace=ws)
+    compare(out, oracle_full(big), "bf16", "B96 Hkv8 after a small-shape init")
+    assert gqa.workspace_errors(ws) == 0
+
+
+@pytest.mark.parametrize("entry", ["dense", "paged", "fused"])
+def test_uninitialised_workspace_is_refused(entry):
+    """A workspace that never went through gqa_workspace_init (here: every byte 0x11, so the
+    counters are not zero) is refused: every output row is NaN, each workgroup counts itself in the
+    header's error word (which, never initialised, starts from whatever the memory held), no counter
+    is touched and the fused call writes no cache row.  After
+    initialisation the same buffer gives the oracle's result."""
+    say(f"uninitialised workspace: {entry}")
+    B, Hq, Hkv, d, L, wg = 5, 32, 4, 128, 700, 29
+    case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", "bf16", seq_lens=(700, 0, 351, 1, 640), seed=43)
+    dv = to_dev(case)
+    shape = gqa.make_shape(B, Hq, Hkv, L, d, gqa.BF16, gqa.BF16, gqa.F32, num_workgroups=wg)
+    ws = torch.full((gqa.workspace_bytes(shape),), 0x11, dtype=torch.uint8, device=DEV)
+    kw = dict(out_dtype=torch.float32, num_workgroups=wg, workspace=ws)
+    if entry == "paged":
+        pg = workloads.paginate(case, 32, seed=44, spare_pages=2)
+        kp, vp, tab = pg["k_pages"].to(DEV), pg["v_pages"].to(DEV), pg["block_table"].to(DEV)
+        call = lambda: gqa.decode_paged(dv["q"], kp, vp, tab, dv["seq_lens"], case["scale"], **kw)
+        want = ref.decode_paged(case["q"], pg["k_pages"], pg["v_pages"], pg["block_table"].numpy(),
+                                case["seq_lens"].numpy(), case["scale"], "all", "bf16", "bf16")
+    elif entry == "fused":
+        g = torch.Generator().manual_seed(45)
+        kn = torch.randn(B, Hkv, d, generator=g).to(torch.bfloat16)
+        vn = torch.randn(B, Hkv, d, generator=g).to(torch.bfloat16)
+        k0 = dv["k"].clone()
+        call = lambda: gqa.decode_append(dv["q"], kn.to(DEV), vn.to(DEV), dv["k"], dv["v"], dv["seq_lens"],
+                                         case["scale"], **kw)
+        pos = (case["seq_lens"] - 1).numpy()
+        wk, wv, _ = ref.append(kn, vn, "bf16", case["k"], case["v"], "bf16", pos)
+        want = ref.decode_all(case["q"], wk, wv, case["seq_lens"].numpy(), case["scale"], "bf16", "bf16")
+    else:
+        call = lambda: gqa.decode(dv["q"], dv["k"], dv["v"], dv["seq_lens"], case["scale"], **kw)
+        want = oracle_full(case)
+    got = call()
+    torch.cuda.synchronize()
+    assert torch.isnan(got).all(), "a refused workspace must give NaN in every output row"
+    # the error word held 0x11111111 like every other byte; each workgroup added one
+    assert gqa.workspace_errors(ws) - 0x11111111 == wg
+    assert (ws[256:COUNTERS_END] == 0x11).all(), "a refused call touched the counters"
+    if entry == "fused":
+        assert torch.equal(dv["k"].view(torch.int16), k0.view(torch.int16)), "a refused call wrote the cache"
+    gqa.init_workspace(ws, shape)
+    got = call()
+    compare(got, want, "bf16", f"{entry} after initialisation")
+    assert gqa.workspace_errors(ws) == 0
 
 
 def test_one_workspace_serves_shapes_in_any_order():
@@ -299,13 +362,38 @@ def test_one_workspace_serves_shapes_in_any_order():
     big = workloads.make_case(2, 8, 2, 128, 4000, "bf16", "bf16", seq_lens=(4000, 3900), seed=40)
     many = workloads.make_case(24, 32, 8, 128, 600, "bf16", "bf16", seq_lens=tuple(range(577, 601)),
                                seed=41)
-    ws = torch.zeros(32 << 20, dtype=torch.uint8, device=DEV)
+    ws = gqa.new_workspace(gqa.make_shape(2, 8, 2, 4000, 128), DEV, 32 << 20)
     for case, wg in ((big, 64), (many, 128), (big, 512), (many, 37)):
         d = to_dev(case)
         out = gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"], case["scale"], out_dtype=torch.float32,
                          num_workgroups=wg, workspace=ws)
         torch.cuda.synchronize()
         compare(out, oracle_full(case), "bf16", f"B{case['B']} after reuse, {wg} workgroups")
+
+
+SOAK = [(3, 16, 4, 128, 2048, "bf16", 37), (2, 64, 8, 128, 3000, "fp8_e4m3", 256), (1, 8, 1, 64, 5000, "bf16", 300),
+        (7, 32, 1, 128, 900, "bf16", 0), (4, 24, 3, 128, 1500, "fp8_e4m3", 4096), (2, 8, 2, 128, 16, "bf16", 2)]
+
+
+@pytest.mark.parametrize("cfg", SOAK, ids=lambda c: "B{}Hq{}Hkv{}d{}L{}-{}-wg{}".format(*c))
+def test_merge_soak_is_bitwise_stable(cfg):
+    """The cross-workgroup merge under repetition: each shape decoded 50 times back to back on one
+    workspace (ragged lengths, so segments are shared by many workgroups and merged by whichever
+    finishes last); every run is compared bitwise with the first, and the first with the oracle.
+    Stops at the first difference."""
+    B, Hq, Hkv, d, L, kd, wg = cfg
+    say(f"merge soak {cfg}")
+    case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", kd, seq_range=(L // 3, L), seed=B * L + wg)
+    dv = to_dev(case)
+    shape = gqa.make_shape(B, Hq, Hkv, L, d, gqa.BF16, gqa._CODE[TORCH[kd]], gqa.F32, num_workgroups=wg)
+    ws = gqa.new_workspace(shape, DEV)
+    outs = [gqa.decode(dv["q"], dv["k"], dv["v"], dv["seq_lens"], case["scale"], out_dtype=torch.float32,
+                       num_workgroups=wg, workspace=ws) for _ in range(50)]
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs[1:], 1):
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32)), f"run {i} differs from run 0"
+    compare(outs[0], oracle_full(case), kd, "soak")
+    assert (ws[8:COUNTERS_END] == 0).all()
 
 
 def test_out_of_range_seq_lens_are_clamped_and_reported():
