@@ -77,31 +77,42 @@ def cpu_model():
 
 
 def cpu_baseline(case, groups_b, paged=None):
-    """Time the fp64 oracle (single thread) on every query head of batch entries [0, groups_b)."""
+    """Time the fp64 oracle on every query head of batch entries [0, groups_b): once on one thread,
+    once with the rows cut over every CPU this process may use (the same C code per row)."""
     from oracle import ref
 
     rows = [(b, h) for b in range(groups_b) for h in range(case["Hq"])]
     sl = case["seq_lens"].numpy()
-    t0 = time.perf_counter()
-    if paged is None:
-        ref.decode_rows(case["q"], case["k"], case["v"], sl, case["scale"], rows, case["q_dtype"],
-                        case["kv_dtype"], case["k_descale"], case["v_descale"])
-    else:
-        ref.decode_paged(case["q"], paged["k_pages"], paged["v_pages"], paged["block_table"].numpy(), sl,
-                         case["scale"], rows, case["q_dtype"], case["kv_dtype"], case["k_descale"],
-                         case["v_descale"])
-    dt = time.perf_counter() - t0
+
+    def run(threads):
+        t0 = time.perf_counter()
+        if paged is None:
+            ref.decode_rows(case["q"], case["k"], case["v"], sl, case["scale"], rows, case["q_dtype"],
+                            case["kv_dtype"], case["k_descale"], case["v_descale"], threads=threads)
+        else:
+            ref.decode_paged(case["q"], paged["k_pages"], paged["v_pages"], paged["block_table"].numpy(), sl,
+                             case["scale"], rows, case["q_dtype"], case["kv_dtype"], case["k_descale"],
+                             case["v_descale"], threads=threads)
+        return time.perf_counter() - t0
+
+    cores = ref.host_threads()
+    dt_all = run(cores)
+    dt_one = run(1)
     elt = 1 if case["kv_dtype"] == "fp8_e4m3" else (4 if case["kv_dtype"] == "f32" else 2)
     kv_bytes = int(sl[:groups_b].sum()) * case["Hkv"] * 2 * case["d"] * elt
-    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    return {"value": round(kv_bytes / dt_all / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"all {case['Hq']} query heads of batch entries 0..{groups_b - 1} "
                       f"({groups_b * case['Hkv']} of {case['B'] * case['Hkv']} (batch, KV head) groups, "
-                      f"{kv_bytes / 1e6:.1f} MB of KV), single-threaded C, {dt:.1f} s, on "
-                      f"{cpu_model() or 'an unnamed CPU'} ({os.cpu_count()} logical CPUs)"}
+                      f"{kv_bytes / 1e6:.1f} MB of KV): {dt_all:.2f} s with the rows cut over {cores} threads, "
+                      f"{dt_one:.1f} s on one",
+            "single_thread": {"value": round(kv_bytes / dt_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "seconds": round(dt_one, 2)},
+            "cpu_model": cpu_model() or "unnamed", "cpus_online": os.cpu_count()}
 
 
 def prefill_cpu_baseline(case, nrows=4000):
-    """Time the fp64 oracle (single thread) on a sample of causal prefill rows, as TFLOP/s."""
+    """Time the fp64 oracle on a sample of causal prefill rows, as TFLOP/s: on one thread and with
+    the rows cut over every CPU this process may use."""
     from oracle import ref
 
     import numpy as np
@@ -112,12 +123,59 @@ def prefill_cpu_baseline(case, nrows=4000):
     for _ in range(nrows):
         random_rows.append((int(gen.integers(w.B)), int(gen.integers(w.Hq)), int(gen.integers(w.S))))
     flops = sum(4 * w.d * (i + 1) for _, _, i in random_rows)
-    t0 = time.perf_counter()
-    ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", True, rows=random_rows)
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 8), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+
+    def run(threads):
+        t0 = time.perf_counter()
+        ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", True, rows=random_rows,
+                    threads=threads)
+        return time.perf_counter() - t0
+
+    cores = ref.host_threads()
+    dt_all = run(cores)
+    dt_one = run(1)
+    return {"value": round(flops / dt_all / 1e12, 8), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{nrows} random (batch, head, position) rows of the same prompt, "
-                      f"{flops / 1e9:.2f} GFLOP, single-threaded C, {dt:.1f} s"}
+                      f"{flops / 1e9:.2f} GFLOP: {dt_all:.2f} s on {cores} threads, {dt_one:.1f} s on one",
+            "single_thread": {"value": round(flops / dt_one / 1e12, 8), "unit": "TFLOP/s", "cores": 1,
+                              "seconds": round(dt_one, 2)},
+            "cpu_model": cpu_model() or "unnamed", "cpus_online": os.cpu_count()}
+
+
+def launch_stats(step, stream, nsteps, per_block=10):
+    """Per-step device time of back-to-back launches, from HIP events on the launch stream around
+    blocks of `per_block` launches: median, p10 and p90 over the blocks (microseconds).  One event
+    pair per block keeps the events' own cost out of the per-launch figure."""
+    import torch
+
+    nblocks = max(10, nsteps // per_block)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nblocks)]
+    i = 0
+    for a, b in ev:
+        a.record(stream)
+        for _ in range(per_block):
+            step(i)
+            i += 1
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 / per_block for a, b in ev)
+    n = len(us)
+    return {"median": round(us[n // 2], 3), "p10": round(us[n // 10], 3), "p90": round(us[(9 * n) // 10], 3),
+            "blocks": n, "launches_per_block": per_block}
+
+
+def end_to_end_us(step, n=50):
+    """Host time of one call issued and completed alone (launch included): median over n calls."""
+    import torch
+
+    t = []
+    for i in range(n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step(i)
+        torch.cuda.synchronize()
+        t.append((time.perf_counter() - t0) * 1e6)
+    t.sort()
+    return round(t[len(t) // 2], 2)
 
 
 def bench_prefill(args):
@@ -153,17 +211,10 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    launch_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    avg_ms = sum(launch_ms) / len(launch_ms)
-    achieved = w.flops / (avg_ms * 1e-3) / 1e12
-    log(f"step {ms_per_step * 1e3:.1f} us wall ({value:.1f} TFLOP/s); kernel avg {avg_ms * 1e3:.1f} us "
-        f"(p10 {launch_ms[len(launch_ms) // 10] * 1e3:.1f}, p90 {launch_ms[9 * len(launch_ms) // 10] * 1e3:.1f}); "
+    lt = launch_stats(lambda i: step(), stream, args.steps, per_block=5)
+    achieved = w.flops / (lt["median"] * 1e-6) / 1e12
+    log(f"step {ms_per_step * 1e3:.1f} us wall ({value:.1f} TFLOP/s); per launch median {lt['median']:.1f} us "
+        f"(p10 {lt['p10']:.1f}, p90 {lt['p90']:.1f}); "
         f"{achieved:.1f} TFLOP/s = {100 * achieved / MFMA_BF16_PEAK_TFLOPS:.1f}% of the bf16 MFMA peak")
     result = {
         "metric": "causal GQA prefill TFLOP/s (bf16)", "value": round(value, 2), "unit": "TFLOP/s",
@@ -174,6 +225,7 @@ def bench_prefill(args):
                    "causal": True, "flops_per_step": w.flops, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "launch_us": lt,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the same prompt")
@@ -257,7 +309,7 @@ def main():
     else:
         shape = gqa.make_shape(w.B, w.Hq, w.Hkv, w.L, w.d, code[w.q_dtype], code[w.kv_dtype],
                                code[w.out_dtype], num_workgroups=args.workgroups)
-    ws = torch.zeros(gqa.workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    ws = gqa.new_workspace(shape, dev)
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
     shape_ref = ctypes.byref(shape)
@@ -316,31 +368,30 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K back-to-back steps between two device synchronisations (host clock)
+    # timed region: K back-to-back steps between two device synchronisations (host clock), with one
+    # HIP event pair on the launch stream around the whole region
     torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    r0.record(stream)
     for i in range(args.steps):
         step(i)
+    r1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    region_us = r0.elapsed_time(r1) * 1e3 / args.steps
 
-    # the kernel's average launch duration for the roofline figure: HIP events around every launch,
-    # recorded on the stream the kernel runs on, over another K steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    launch_ms = sorted(a.elapsed_time(b) for a, b in ev)
-    avg_launch_ms = sum(launch_ms) / len(launch_ms)
-    achieved = kv_bytes / (avg_launch_ms * 1e-3) / 1e9
-    log(f"step {ms_per_step * 1e3:.1f} us wall ({value:.0f} GB/s); kernel avg {avg_launch_ms * 1e3:.1f} us "
-        f"(p10 {launch_ms[len(launch_ms) // 10] * 1e3:.1f}, p90 {launch_ms[9 * len(launch_ms) // 10] * 1e3:.1f}); "
-        f"{achieved:.0f} GB/s = {100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s")
+    # per-launch device time for the roofline figure: the median over blocks of back-to-back launches
+    lt = launch_stats(step, stream, max(args.steps, 200))
+    lt["region_avg"] = round(region_us, 3)
+    achieved = kv_bytes / (lt["median"] * 1e-6) / 1e9
+    e2e = end_to_end_us(step)
+    log(f"step {ms_per_step * 1e3:.1f} us wall ({value:.0f} GB/s); per launch median {lt['median']:.1f} us "
+        f"(p10 {lt['p10']:.1f}, p90 {lt['p90']:.1f}; timed-region average {region_us:.1f}); "
+        f"{achieved:.0f} GB/s = {100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s; one call alone, launch included, "
+        f"{e2e:.1f} us")
 
     # achievable streaming-read bandwidth on one cache copy, for context
     sink = torch.empty(gqa.lib.gqa_stream_read_sink_words(), dtype=torch.int32, device=dev)
@@ -385,6 +436,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
+        "launch_us": lt,
+        "end_to_end_us": e2e,
+        "calibration_read_gbs": round(calib, 1),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the same workload")
