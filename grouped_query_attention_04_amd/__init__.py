@@ -61,6 +61,7 @@ class PagedShape(ctypes.Structure):
 
 
 EXPORTS = ["gqa_shape_check", "gqa_decode_workspace_bytes", "gqa_workspace_init", "gqa_decode",
+           "gqa_decode_static",
            "gqa_paged_shape_check", "gqa_decode_paged_workspace_bytes", "gqa_paged_workspace_init",
            "gqa_decode_paged", "gqa_append_kv", "gqa_append_kv_paged", "gqa_decode_append",
            "gqa_decode_append_paged", "gqa_prefill_shape_check",
@@ -83,6 +84,8 @@ def _load():
     lib.gqa_workspace_init.restype = ctypes.c_int
     lib.gqa_decode.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, pS, vp, sz, vp]
     lib.gqa_decode.restype = ctypes.c_int
+    lib.gqa_decode_static.argtypes = [vp, vp, vp, vp, ctypes.c_float, vp, pS, vp]
+    lib.gqa_decode_static.restype = ctypes.c_int
     pP = ctypes.POINTER(PagedShape)
     lib.gqa_paged_shape_check.argtypes = [pP]
     lib.gqa_paged_shape_check.restype = ctypes.c_int

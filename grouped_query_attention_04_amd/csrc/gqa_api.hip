@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "gqa.h"
 #include "gqa_append.h"
@@ -185,6 +186,35 @@ gqa_status_t dispatch_f32(int G, int out_dtype, int grid, const gqa::Params& prm
   return dispatch_f32_out<D, 32>(out_dtype, grid, prm, st);
 }
 
+// Scratch of gqa_decode_static: a file-scope device array, one copy per GPU, that stands in for the
+// caller's workspace.  Host code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory); it uses the device address hipGetSymbolAddress returns for the
+// current device, kept per device in static_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[GQA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex static_scratch_mu;
+void* static_scratch_ptr[kMaxDevices];  // guarded by static_scratch_mu; set once per device
+
+// The device address of this GPU's scratch, set up on the device's first call: the address looked
+// up once, and the workspace initialised (header tag, counters cleared) by a kernel on `stream`, so
+// the decode enqueued after it on the same stream finds it ready.  nullptr on a HIP error.
+void* static_scratch(hipStream_t stream, int* dev_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  *dev_out = dev;
+  std::lock_guard<std::mutex> lock(static_scratch_mu);
+  if (static_scratch_ptr[dev]) return static_scratch_ptr[dev];
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  const int n = (int)((kHeaderBytes + kMaxUnits * sizeof(uint32_t)) / sizeof(uint32_t));
+  hipLaunchKernelGGL(gqa::init_workspace_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
+                     static_cast<uint32_t*>(ptr), n);
+  if (hipGetLastError() != hipSuccess) return nullptr;
+  static_scratch_ptr[dev] = ptr;
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -253,6 +283,24 @@ gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                       : dispatch_f32<128>(prm.G, s->out_dtype, grid, prm, hs);
   }
   return dispatch_mfma_dtype<false>(s->kv_dtype, s->d, prm.G, s->out_dtype, grid, prm, hs);
+}
+
+gqa_status_t gqa_decode_static(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* seq_lens, float scale, void* out, const gqa_shape_t* s,
+                               void* stream) {
+  // every check gqa_decode makes before touching the device, plus the scratch's size limit
+  if (!q || !k_cache || !v_cache || !seq_lens || !out || !s) return GQA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(seq_lens, 4))
+    return GQA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARG;
+  const gqa_status_t st = gqa_shape_check(s);
+  if (st != GQA_OK) return st;
+  if (plan(s).total > (size_t)GQA_STATIC_SCRATCH_BYTES) return GQA_ERR_WORKSPACE;
+  int dev = -1;
+  void* ws = static_scratch((hipStream_t)stream, &dev);
+  if (!ws) return GQA_ERR_HIP;
+  return gqa_decode(q, k_cache, v_cache, seq_lens, scale, out, s, ws, GQA_STATIC_SCRATCH_BYTES, stream);
 }
 
 gqa_status_t gqa_paged_shape_check(const gqa_paged_shape_t* s) {

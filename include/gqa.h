@@ -104,6 +104,24 @@ gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
+ * Decode without a caller workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same operation, arguments,
+ * checks and kernels as gqa_decode, but the workspace is a fixed array of GQA_STATIC_SCRATCH_BYTES
+ * inside the library, one per GPU, held until the process ends; no call allocates or frees memory.
+ * The first call on a device looks the array up and initialises it with a small kernel on `stream`;
+ * later calls find its counters back at zero.  Shapes whose workspace (gqa_decode_workspace_bytes)
+ * exceeds GQA_STATIC_SCRATCH_BYTES return GQA_ERR_WORKSPACE before any HIP call; a HIP error while
+ * setting the array up returns GQA_ERR_HIP.  All calls on one GPU share its array, so calls that
+ * overlap in time on one GPU (on different streams or from several threads without ordering) race
+ * and give undefined results: order them on one stream.
+ */
+#define GQA_STATIC_SCRATCH_BYTES (24u << 20)
+
+gqa_status_t gqa_decode_static(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* seq_lens, float scale, void* out, const gqa_shape_t* shape,
+                               void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * Paged cache.  Serving engines keep the cache in fixed-size pages handed out on demand ("Grouped
  * Query Attention: Why 8 KV Heads Decide Your Batch Size", section "What should you do about it?",
  * lists paged allocation among the levers; "Grouped-Query Attention: How Sharing KV Heads Shrinks
