@@ -85,7 +85,8 @@ gqa_status_t dispatch_mfma_out(int out_dtype, int grid, const gqa::Params& prm, 
 template <int D, bool FP8, bool PAGED, bool APPEND>
 gqa_status_t dispatch_mfma(int G, int out_dtype, int grid, const gqa::Params& prm, hipStream_t st) {
   if (G <= 16) return dispatch_mfma_out<D, 1, FP8, PAGED, APPEND>(out_dtype, grid, prm, st);
-  return dispatch_mfma_out<D, 2, FP8, PAGED, APPEND>(out_dtype, grid, prm, st);
+  if (G <= 32) return dispatch_mfma_out<D, 2, FP8, PAGED, APPEND>(out_dtype, grid, prm, st);
+  return dispatch_mfma_out<D, 4, FP8, PAGED, APPEND>(out_dtype, grid, prm, st);
 }
 
 template <bool PAGED, bool APPEND = false>
@@ -228,11 +229,13 @@ gqa_status_t gqa_shape_check(const gqa_shape_t* s) {
   if (!std::isfinite(s->k_descale) || !std::isfinite(s->v_descale)) return GQA_ERR_INVALID_ARG;
   if (s->num_workgroups < 0 || s->num_workgroups > kMaxWorkgroups) return GQA_ERR_INVALID_ARG;
   if (s->d != 64 && s->d != 128) return GQA_ERR_UNSUPPORTED;
-  if (s->Hq / s->Hkv > 32) return GQA_ERR_UNSUPPORTED;
   if (s->out_dtype != GQA_F32 && s->out_dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
   const bool f32_path = s->q_dtype == GQA_F32 && s->kv_dtype == GQA_F32;
   const bool mfma_path = s->q_dtype == GQA_BF16 && (s->kv_dtype == GQA_BF16 || s->kv_dtype == GQA_FP8_E4M3);
   if (!f32_path && !mfma_path) return GQA_ERR_UNSUPPORTED;
+  // group sizes: up to 64 query heads per KV head on the matrix cores (four 16-row query tiles), up
+  // to 32 on the f32 vector path
+  if (s->Hq / s->Hkv > (mfma_path ? 64 : 32)) return GQA_ERR_UNSUPPORTED;
   // per-(batch, KV head) cache slices are addressed with 32-bit byte offsets
   if ((long long)s->L * s->d * elt_bytes(s->kv_dtype) >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
   // the tile space (tiles of 16 positions per batch entry and KV head) is counted with 32-bit ints

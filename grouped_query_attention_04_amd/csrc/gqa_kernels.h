@@ -226,6 +226,78 @@ struct Piece {
   int slot;        // 0: the piece starts this workgroup's range, 1: it ends it
 };
 
+// Log-sum-exp merge of a segment's npc published pieces (those of workgroups wfirst ..
+// wfirst + npc - 1, in that order) into the output rows.  Every thread carries the running (max,
+// sum, output) of NI items (4 consecutive columns of one query row each).  The pieces' partials
+// stream through PB register sets: piece k is merged, then the loads of piece k + PB go out, so PB
+// pieces are always in flight and the merge pays one load latency, not one per group of pieces.
+// The piece loop is uniform, so each piece's buffer descriptors stay scalar.  Every load carries
+// agent scope (sc1), the form of a relaxed agent-scope atomic load.
+template <int D, typename OutT, int NTH, int NI, int PB>
+__device__ __forceinline__ void merge_pieces(const Params& p, OutT* out, int nitems, int wfirst, int npc,
+                                             int first_slot) {
+  const int tid = threadIdx.x;
+  const int G = p.G;
+  float acc_m[NI], acc_l[NI];
+  f32x4_t acc_o[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    acc_m[i] = -INFINITY;
+    acc_l[i] = 0.f;
+    acc_o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  struct PieceRegs {
+    uint32_t m[NI], l[NI];
+    u32x4_t o[NI];
+  };
+  auto load_piece = [&](PieceRegs& R, int k) __attribute__((always_inline)) {
+    if (k >= npc) return;
+    const size_t sl = (size_t)uniform((wfirst + k) * 2 + (k == 0 ? first_slot : 0));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.part_o + sl * G * D, G * D * 4);
+    const __amdgpu_buffer_rsrc_t rml = make_rsrc(p.part_ml + sl * G * 2, G * 2 * 4);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int item = tid + i * NTH;
+      if (i > 0 && uniform(i * NTH) >= nitems) break;  // item slots past the group's rows
+      const int g = (4 * (item < nitems ? item : 0)) / D;
+      // two 4-byte loads: element 1 of a 64-bit buffer load's vector result is not reliable here
+      R.m[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rml, g * 8, 0, kAgentScope);
+      R.l[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rml, g * 8 + 4, 0, kAgentScope);
+      R.o[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, item * 16, 0, kAgentScope));
+    }
+  };
+  auto merge_piece = [&](const PieceRegs& R) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (i > 0 && uniform(i * NTH) >= nitems) break;  // not loaded: never stored either
+      const float m = __builtin_bit_cast(float, R.m[i]);
+      const float l = __builtin_bit_cast(float, R.l[i]);
+      const float mn = fmaxf(acc_m[i], m);
+      const float a = __builtin_amdgcn_exp2f(acc_m[i] - mn);
+      const float sc = __builtin_amdgcn_exp2f(m - mn);
+      acc_l[i] = acc_l[i] * a + l * sc;
+      acc_o[i] = acc_o[i] * a + __builtin_bit_cast(f32x4_t, R.o[i]) * sc;
+      acc_m[i] = mn;
+    }
+  };
+  PieceRegs R[PB];
+#pragma unroll
+  for (int u = 0; u < PB; ++u) load_piece(R[u], u);
+  for (int k0 = 0; k0 < npc; k0 += PB) {
+#pragma unroll
+    for (int u = 0; u < PB; ++u) {
+      if (k0 + u >= npc) break;
+      merge_piece(R[u]);
+      load_piece(R[u], k0 + u + PB);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int item = tid + i * NTH;
+    if (item < nitems) store_out4(out + 4 * item, acc_o[i] * (p.v_descale / acc_l[i]));
+  }
+}
+
 template <int GT, int D, int NW, typename OutT>
 __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r, const Piece& pc,
                                Shared& sh) {
@@ -302,72 +374,20 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
   // workgroups completed before theirs.  The compiler fence keeps the loads below the barrier.
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
-  // Last piece of the segment: log-sum-exp merge of its pieces in workgroup order.  Every thread
-  // carries the running (max, sum, output) of its NI items.  The pieces' partials stream through PB
-  // register sets: piece k is merged, then the loads of piece k + PB go out, so PB pieces are always
-  // in flight and the merge pays one load latency, not one per group of pieces.  The piece loop is
-  // uniform, so each piece's buffer descriptor stays scalar.
-  constexpr int NI = (GT * D / 4 + NTH - 1) / NTH;
-  constexpr int PB = NI > 2 ? 4 : 8;  // pieces in flight (registers: 6 * NI per piece)
+  // Last piece of the segment: log-sum-exp merge of its pieces in workgroup order.  When the
+  // group's items fit one per thread (G * D / 4 <= NTH, e.g. G <= 8 at D = 128), the pieces stream
+  // through more register sets, so that up to 16 pieces' partials are in flight at once.
   const int npc = wlast - wfirst + 1;
   // Slot of the segment's piece in workgroup w: workgroups after the first hold the segment from
   // their first tile on, i.e. in slot 0; the first one holds it in slot 1 when the segment starts
   // after its first tile.
   const int first_slot = uniform(pc.s > range_lo(wfirst, r.T, r.weff) ? 1 : 0);
-  float acc_m[NI], acc_l[NI];
-  f32x4_t acc_o[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    acc_m[i] = -INFINITY;
-    acc_l[i] = 0.f;
-    acc_o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-  struct PieceRegs {
-    float m[NI], l[NI];
-    u32x4_t o[NI];
-  };
-  auto load_piece = [&](PieceRegs& R, int k) __attribute__((always_inline)) {
-    if (k >= npc) return;
-    const size_t sl = (size_t)uniform((wfirst + k) * 2 + (k == 0 ? first_slot : 0));
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.part_o + sl * G * D, G * D * 4);
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int item = tid + i * NTH;
-      if (i > 0 && uniform(i * NTH) >= nitems) break;  // item slots past the group's rows
-      const int g = (4 * (item < nitems ? item : 0)) / D;
-      R.m[i] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      R.l[i] = __hip_atomic_load(p.part_ml + (sl * G + g) * 2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      R.o[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, item * 16, 0, kAgentScope));
-    }
-  };
-  auto merge_piece = [&](const PieceRegs& R) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if (i > 0 && uniform(i * NTH) >= nitems) break;  // not loaded: never stored either
-      const float mn = fmaxf(acc_m[i], R.m[i]);
-      const float a = __builtin_amdgcn_exp2f(acc_m[i] - mn);
-      const float sc = __builtin_amdgcn_exp2f(R.m[i] - mn);
-      acc_l[i] = acc_l[i] * a + R.l[i] * sc;
-      acc_o[i] = acc_o[i] * a + __builtin_bit_cast(f32x4_t, R.o[i]) * sc;
-      acc_m[i] = mn;
-    }
-  };
-  PieceRegs R[PB];
-#pragma unroll
-  for (int u = 0; u < PB; ++u) load_piece(R[u], u);
-  for (int k0 = 0; k0 < npc; k0 += PB) {
-#pragma unroll
-    for (int u = 0; u < PB; ++u) {
-      if (k0 + u >= npc) break;
-      merge_piece(R[u]);
-      load_piece(R[u], k0 + u + PB);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int item = tid + i * NTH;
-    if (item < nitems) store_out4(out + 4 * item, acc_o[i] * (p.v_descale / acc_l[i]));
-  }
+  constexpr int NI = (GT * D / 4 + NTH - 1) / NTH;
+  if (NI > 1 && nitems <= NTH)
+    merge_pieces<D, OutT, NTH, 1, 16>(p, out, nitems, wfirst, npc, first_slot);
+  else
+    merge_pieces<D, OutT, NTH, NI, (NI > 4 ? 2 : NI > 2 ? 4 : NI == 2 ? 8 : 16)>(p, out, nitems, wfirst, npc,
+                                                                              first_slot);
   if (tid == 0) __hip_atomic_store(p.counters + bj, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -423,7 +443,7 @@ __device__ void for_each_piece(const Params& p, const Range& r, Body&& body) {
 //
 // PAGED: the cache lives in pages of block_size (a power of two, at least TILE) positions, so a tile
 // never straddles two pages.  Each register set of the pipeline carries the page-table entry of the
-// tile it will receive next (two tiles on in the wave's order): the entry is loaded just ahead of
+// tile it will receive next (NBUF tiles on in the wave's order): the entry is loaded just ahead of
 // the set's own tile loads and moved to a scalar register when that tile is computed, after the
 // wait for the tile, so it never costs a wait of its own.  The page's buffer descriptors are built
 // per tile; a page number outside the pool yields a descriptor of zero bytes.
@@ -440,6 +460,11 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
   constexpr int CPR = D / 8;          // 16-byte bf16 chunks per row of the LDS V tile
   constexpr int VTILE = TILE * D * 2;            // bytes of one LDS V tile (bf16)
   constexpr int GT = 16 * NT;
+  // register sets of the load pipeline.  Two for both cache formats: keeping three or four fp8 tiles
+  // in flight (the bytes in flight of two bf16 tiles) was measured slower on the long fp8 cache
+  // (B2 Hq64 Hkv8 L32768: 30.9 us with two sets, 31.3 with three, 32.0 with four, 33.2 with six),
+  // and three bf16 sets slower on every bf16 workload (141.2 -> 142.4 us on the 70B layer).
+  constexpr int NBUF = 2;
   using Epi = EpiLayout<GT, D, NW>;
   constexpr int SMEM = (NW * VTILE > Epi::kBytes) ? NW * VTILE : Epi::kBytes;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
@@ -564,7 +589,7 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
           t0 &= (1u << p.block_shift) - 1;  // position within the page
         }
       }
-      if constexpr (PAGED) R.pg = load_entry(it + 2);
+      if constexpr (PAGED) R.pg = load_entry(it + NBUF);
 #pragma unroll
       for (int x = 0; x < NK; ++x) {  // 16-byte column block x of this lane's quad, token row r
         const uint32_t off = (t0 + r) * ROWB + x * 64 + q * 16;
@@ -730,19 +755,23 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
       }
     };
 
-    // ---- software pipeline: the next tile's loads are in flight while this tile is computed
-    Regs A, B;
+    // ---- software pipeline: the loads of the next NBUF - 1 tiles are in flight while this tile is
+    //      computed; register set u receives tiles u, u + NBUF, ...  (unrolled by NBUF, so every set
+    //      is fixed at compile time)
+    Regs R[NBUF];
     if constexpr (PAGED) {
-      A.page = uniform(load_entry(0));
-      B.page = uniform(load_entry(1));
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) R[u].page = uniform(load_entry(u));
     }
-    issue(A, 0);
-    for (int it = 0; it < mine; it += 2) {
-      issue(B, it + 1);
-      compute(A, it);
-      if (it + 1 >= mine) break;
-      issue(A, it + 2);
-      compute(B, it + 1);
+#pragma unroll
+    for (int u = 0; u < NBUF - 1; ++u) issue(R[u], u);
+    for (int it = 0; it < mine; it += NBUF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        if (it + u >= mine) break;
+        issue(R[(u + NBUF - 1) % NBUF], it + u + NBUF - 1);
+        compute(R[u], it + u);
+      }
     }
 
     // ---- wave state -> LDS (canonical layout), then the shared epilogue

@@ -31,7 +31,8 @@
  * bf16 / fp8-e4m3 / {bf16, f32}.  The fp8 cache is the OCP e4m3fn format with per-tensor descales
  * (real value = stored * descale), as in "Grouped-Query Attention: How Sharing KV Heads Shrinks
  * Inference Memory", section "FP8 KV cache: the other factor of two".  Head dims: 64 and 128.
- * Group sizes: G = Hq / Hkv in [1, 32].  Accumulation is fp32; a bf16 out is rounded to nearest even.
+ * Group sizes: G = Hq / Hkv in [1, 64] for bf16 and fp8 caches, [1, 32] for f32 caches.  Accumulation
+ * is fp32; a bf16 out is rounded to nearest even.
  *
  * Ownership and threading.  The caller owns every buffer, the workspace included.  The library never
  * allocates or frees device memory and keeps no mutable global state besides cached device

@@ -48,6 +48,9 @@ def test_valid_shapes_pass():
     assert gqa.shape_check(_shape(d=128, q_dtype=gqa.BF16, kv_dtype=gqa.BF16)) == 0
     assert gqa.shape_check(_shape(d=128, q_dtype=gqa.BF16, kv_dtype=gqa.FP8_E4M3, out_dtype=gqa.F32)) == 0
     assert gqa.shape_check(_shape(Hq=32, Hkv=1, q_dtype=gqa.BF16, kv_dtype=gqa.BF16)) == 0
+    assert gqa.shape_check(_shape(Hq=64, Hkv=1, q_dtype=gqa.BF16, kv_dtype=gqa.BF16)) == 0
+    assert gqa.shape_check(_shape(Hq=128, Hkv=2, q_dtype=gqa.BF16, kv_dtype=gqa.FP8_E4M3)) == 0
+    assert gqa.shape_check(_shape(Hq=32, Hkv=1)) == 0      # f32 cache: up to 32
     assert gqa.shape_check(_shape(Hq=6, Hkv=2, num_workgroups=7)) == 0
     # the largest per-head slice: L * d * bytes just under 2^31
     for L, kv in [((1 << 23) - 1, gqa.BF16), ((1 << 24) - 1, gqa.FP8_E4M3)]:
@@ -61,7 +64,8 @@ def test_valid_shapes_pass():
     (dict(q_dtype=7), 1),                   # unknown dtype code
     (dict(num_workgroups=-1), 1), (dict(num_workgroups=70000), 1),
     (dict(d=96), 2), (dict(d=256), 2),      # head dims outside {64, 128}
-    (dict(Hq=66, Hkv=1), 2),                # group larger than 32
+    (dict(Hq=33, Hkv=1), 2),                # f32 cache: group larger than 32
+    (dict(Hq=65, Hkv=1, q_dtype=gqa.BF16, kv_dtype=gqa.BF16), 2),   # group larger than 64
     (dict(q_dtype=gqa.F32, kv_dtype=gqa.BF16), 2),
     (dict(q_dtype=gqa.BF16, kv_dtype=gqa.F32), 2),
     (dict(q_dtype=gqa.FP8_E4M3, kv_dtype=gqa.FP8_E4M3), 2),

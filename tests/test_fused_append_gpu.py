@@ -165,7 +165,8 @@ def test_fused_is_bitwise_the_two_calls(kv, paged_bs, wg):
     assert _bitwise(o1, o2), "outputs differ"
 
 
-FUSED_FULL = [(3, None), (3, 16), (2, None), (2, 32), ("4-gqa", 64), (5, None), (5, 64)]
+FUSED_FULL = [(3, None), (3, 16), (2, None), (2, 32), ("4-gqa", 64), ("4-mqa64", None), ("4-mqa64", 16),
+              (5, None), (5, 64)]
 
 
 @pytest.mark.parametrize("wid,paged_bs", FUSED_FULL, ids=lambda x: str(x))

@@ -187,6 +187,17 @@ def test_repeat_kv_then_mha_matches_oracle(Hkv):
     np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(64, 1), (128, 2), (48, 1)])
+def test_repeat_kv_then_mha_matches_oracle_large_groups(Hq, Hkv):
+    """Groups of 48 and 64 query heads per KV head (the multi-query end of a 64-head model)."""
+    q, k, v, sl = _case_f64(31 + Hq, Hq=Hq, Hkv=Hkv)
+    G = Hq // Hkv
+    got = ref.decode(q.float().numpy(), k.float().numpy(), v.float().numpy(), sl, 0.3)
+    want = _mha_per_head(q.float().double(), _repeat_kv(k.float().double(), G),
+                         _repeat_kv(v.float().double(), G), sl, 0.3)
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+
+
 def test_group_size_one_is_plain_mha():
     q, k, v, sl = _case_f64(5, Hq=6, Hkv=6)
     q, k, v = (x.float().double() for x in (q, k, v))

@@ -44,6 +44,7 @@ PAGED_SMALL = [
     (2, 8, 2, 64, 700, (700, 1), 32, 256),
     (2, 8, 8, 128, 600, (513, 600), 64, 0),       # G = 1
     (2, 32, 1, 128, 520, (520, 257), 16, 256),    # G = 32
+    (2, 64, 1, 128, 520, (520, 257), 16, 64),     # G = 64
     (1, 10, 2, 128, 900, (899,), 128, 7),         # G = 5
     (2, 16, 2, 128, 5000, (5000, 4111), 16, 1),   # one workgroup: > 64 tiles per wave and piece
     (2, 16, 2, 128, 9000, (9000, 8999), 256, 3),  # three page windows per wave and piece
@@ -110,7 +111,7 @@ def test_paged_out_of_pool_entry_reads_zeros():
     compare(got, oracle_paged(case, zpg, table=ztab), "bf16", "zero page")
 
 
-@pytest.mark.parametrize("wid,bs", [(3, 16), (5, 64), (2, 32)])
+@pytest.mark.parametrize("wid,bs", [(3, 16), (5, 64), (2, 32), ("4-gqa", 128), ("4-mqa64", 16)])
 def test_paged_workload_parity(wid, bs):
     """Full-size workloads in paged form, library's workgroup count, every output row against the
     oracle."""

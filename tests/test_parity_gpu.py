@@ -104,6 +104,9 @@ SMALL = [
     (1, 10, 2, 128, 900, (899,), 512),         # G = 5
     (2, 32, 2, 128, 1000, (1000, 640), 256),   # G = 16
     (1, 64, 8, 128, 2048, (2048,), 0),
+    (2, 64, 1, 128, 520, (520, 257), 256),     # G = 64 (all query heads on one KV head)
+    (1, 128, 2, 64, 700, (699,), 0),           # G = 64, head dim 64
+    (3, 48, 1, 128, 333, (333, 0, 17), 7),     # G = 48
 ]
 
 
@@ -113,6 +116,11 @@ def test_small_parity(cfg, qd, kd):
     B, Hq, Hkv, d, L, sl, wg = cfg
     say(f"small parity {cfg} q={qd} kv={kd}")
     case = workloads.make_case(B, Hq, Hkv, d, L, qd, kd, seq_lens=sl, seed=hash(cfg) % 10000)
+    if kd == "f32" and Hq // Hkv > 32:      # the f32 vector path takes groups of up to 32
+        with pytest.raises(gqa.GqaError) as e:
+            run(case, workgroups=wg)
+        assert e.value.code == 2
+        return
     want = oracle_full(case)
     compare(run(case, workgroups=wg), want, kd, "native out")
     compare(run(case, out_dtype="f32", workgroups=wg), want, kd, "f32 out")
@@ -431,7 +439,7 @@ def rows_off(got, want, kv_dtype):
     return [tuple(int(x) for x in i) for i in np.argwhere(err > ABS_GATE[kv_dtype])]
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, "4-mha", "4-gqa", "4-mqa", 5, "3-tp8", "3-d64"])
+@pytest.mark.parametrize("wid", [1, 2, 3, "4-mha", "4-gqa", "4-mqa", "4-mqa64", 5, "3-tp8", "3-d64"])
 def test_workload_parity(wid):
     """Each named workload at full size, in the launch configuration the benchmark times (library's
     workgroup count); every (b, h) output row against the oracle."""
@@ -497,10 +505,28 @@ def _random_shapes(n, seed):
     return out
 
 
-@pytest.mark.parametrize("cfg", _random_shapes(24, 7), ids=lambda c: "B{}Hq{}Hkv{}d{}L{}-{}-wg{}".format(*c[:5], c[6], c[7]))
+def _random_large_groups(n, seed):
+    """Group sizes 33..64 (the four-tile query path), bf16 and fp8 caches."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 3]))
+        G = int(rng.integers(33, 65))
+        d = int(rng.choice([64, 128]))
+        B = int(rng.integers(1, 5))
+        L = int(rng.integers(1, 1200))
+        sl = tuple(int(x) for x in rng.integers(0, L + 1, size=B))
+        kd = str(rng.choice(["bf16", "fp8_e4m3"]))
+        wg = int(rng.choice([0, 1, 5, 37, 256]))
+        out.append((B, G * Hkv, Hkv, d, L, sl, kd, wg))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_shapes(24, 7) + _random_large_groups(8, 8),
+                         ids=lambda c: "B{}Hq{}Hkv{}d{}L{}-{}-wg{}".format(*c[:5], c[6], c[7]))
 def test_random_shapes(cfg):
-    """Seeded random shapes (any group size 1..32, odd KV head counts, empty and ragged sequences,
-    odd workgroup counts, every cache dtype) against the oracle."""
+    """Seeded random shapes (any group size 1..64, odd KV head counts, empty and ragged sequences,
+    odd workgroup counts, every cache dtype; f32 caches only up to 32) against the oracle."""
     B, Hq, Hkv, d, L, sl, kd, wg = cfg
     qd = "f32" if kd == "f32" else "bf16"
     say(f"random shape {cfg}")

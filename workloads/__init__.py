@@ -63,6 +63,10 @@ WORKLOADS = {
                       seq_lens=(4096,) * 8, seed=1004),
     "4-mqa": Workload("sweep B8 Hq32 Hkv1 d128 L4096", 8, 32, 1, 128, 4096, "bf16", "bf16",
                       seq_lens=(4096,) * 8, seed=1004),
+    # the group-size sweep's shape with all 64 query heads of a 70B-class model on one KV head (the
+    # multi-query end of the 70B grouping)
+    "4-mqa64": Workload("sweep B8 Hq64 Hkv1 d128 L4096", 8, 64, 1, 128, 4096, "bf16", "bf16",
+                        seq_lens=(4096,) * 8, seed=1004),
     5: Workload("long-fp8 B2 Hq64 Hkv8 d128 L32768", 2, 64, 8, 128, 32768, "bf16", "fp8_e4m3",
                 seq_lens=(32768, 30000), seed=1005),
     # one rank's share of the 70B-layer step under tensor parallelism of degree 8: one KV head and
