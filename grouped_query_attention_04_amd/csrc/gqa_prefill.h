@@ -9,7 +9,8 @@
 // Work decomposition.  A workgroup owns one (batch b, KV head j, block of BM query positions) and all
 // G query heads of the group, so every K/V tile it stages in LDS serves G heads at once -- the
 // grouping is used, not expanded (same page, the repeat_kv discussion).  Its 256 rows (G heads x BM
-// positions, BM = 256 / G) are split over NW waves of NT 16-row tiles each.  Keys are taken
+// positions, BM = floor(256 / G), and 256 - G * BM padding rows when G does not divide 256) are split
+// over NW waves of NT 16-row tiles each.  Keys are taken
 // in blocks of KB through two LDS buffers: while the waves compute on one block, the next one is
 // being stored into the other, and the global loads of the block after it are in flight in
 // registers.
@@ -61,7 +62,7 @@ struct PrefillParams {
   const void* v;
   void* out;      // [B][Hq][S][D] OutT
   int B, Hq, Hkv, S, G;
-  int bm_shift;   // BM = 1 << bm_shift query positions per workgroup (BM * G = 256 rows)
+  int bm;         // BM = floor(256 / G) query positions per workgroup (BM * G <= 256 rows)
   int nqb;        // query blocks per (b, j)
   float qk_scale; // |scale| * log2(e), positive (1 * log2(e) for a zero scale)
   uint32_t q_and; // applied to each 32-bit word (two bf16) of q: all ones, or 0 for a zero scale
@@ -91,24 +92,38 @@ prefill_mfma_kernel(PrefillParams p) {
   const int qb = p.nqb - 1 - (int)(blockIdx.x / nbj);
   const int bj = (int)(blockIdx.x % nbj);
   const int b = bj / p.Hkv, j = bj % p.Hkv;
-  const int BM = 1 << p.bm_shift;
+  const int BM = p.bm;
+  const int nrows = p.G * BM;  // rows of the workgroup that hold a (head, position); 256 - nrows pad
   const int w = uniform((int)threadIdx.x / 64);
   const int l = threadIdx.x % 64;
   const int q = l / 16;
   const int r = l % 16;
 
-  // the wave's rows: row rho = RW w + 16 nt + r is head g = rho / BM, position qb * BM + rho % BM
+  // the wave's rows: row rho = RW w + 16 nt + r is head g = rho / BM, position qb * BM + rho % BM;
+  // rows past nrows (when G does not divide 256) are padding: position S, a zero query, never stored
   int pos[NT];
   int head[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int rho = RW * w + 16 * nt + r;
-    head[nt] = j * p.G + (rho >> p.bm_shift);
-    pos[nt] = qb * BM + (rho & (BM - 1));
+    head[nt] = j * p.G + (rho < nrows ? rho / BM : 0);
+    pos[nt] = rho < nrows ? qb * BM + rho % BM : p.S;
   }
-  // positions covered by the wave (for skipping blocks it cannot see) and by the workgroup
-  const int wave_lo = uniform(qb * BM + ((RW * w) & (BM - 1)));
-  const int wave_hi = uniform(min(p.S - 1, wave_lo + min(RW, BM) - 1));
+  // positions covered by the wave (for skipping blocks it cannot see): its real rows r0 .. r1 cover
+  // positions r0 % BM .. r1 % BM of one head, or (when they cross to the next head) the whole block
+  const int r0 = RW * w, r1 = min(RW * w + RW, nrows) - 1;
+  int lo_rel = 0, hi_rel = -1;  // no real row: every block is skipped
+  if (r1 >= r0) {
+    if (r0 / BM == r1 / BM) {
+      lo_rel = r0 % BM;
+      hi_rel = r1 % BM;
+    } else {
+      lo_rel = 0;
+      hi_rel = BM - 1;
+    }
+  }
+  const int wave_lo = uniform(qb * BM + lo_rel);
+  const int wave_hi = uniform(hi_rel < 0 ? -1 : min(p.S - 1, qb * BM + hi_rel));
   const int wg_hi = min(p.S, (qb + 1) * BM);  // exclusive
   const int nkb = CAUSAL ? (wg_hi + KB - 1) / KB : (p.S + KB - 1) / KB;
 

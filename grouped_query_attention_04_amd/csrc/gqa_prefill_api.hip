@@ -13,7 +13,6 @@ namespace {
 
 using gqa_host::aligned;
 using gqa_host::known_dtype;
-using gqa_host::log2_exact;
 
 constexpr int kPrefillWaves = 8;  // waves per prefill workgroup (256 rows: 16 * 16 / waves each)
 constexpr int kPrefillKeys = 64;  // keys per prefill LDS block
@@ -31,11 +30,11 @@ gqa_status_t gqa_prefill_shape_check(const gqa_prefill_shape_t* s) {
   if (s->dtype != GQA_BF16) return GQA_ERR_UNSUPPORTED;
   if (s->out_dtype != GQA_BF16 && s->out_dtype != GQA_F32) return GQA_ERR_UNSUPPORTED;
   if (s->d != 64 && s->d != 128) return GQA_ERR_UNSUPPORTED;
-  const int shift = log2_exact(s->Hq / s->Hkv);
-  if (shift < 0 || shift > 5) return GQA_ERR_UNSUPPORTED;  // G a power of two, at most 32
+  const int G = s->Hq / s->Hkv;
+  if (G > 64) return GQA_ERR_UNSUPPORTED;  // any group size up to 64 query heads per KV head
   // per-(batch, KV head) K/V slices are addressed with 32-bit byte offsets
   if ((long long)s->S * s->d * 2 >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
-  const long long nqb = ((long long)s->S * (s->Hq / s->Hkv) + 255) / 256;
+  const long long nqb = ((long long)s->S + 256 / G - 1) / (256 / G);
   if (nqb * s->B * s->Hkv >= (1ll << 31)) return GQA_ERR_UNSUPPORTED;
   return GQA_OK;
 }
@@ -57,8 +56,8 @@ gqa_status_t gqa_prefill(const void* q, const void* k, const void* v, float scal
   pp.Hkv = s->Hkv;
   pp.S = s->S;
   pp.G = s->Hq / s->Hkv;
-  pp.bm_shift = 8 - log2_exact(pp.G);  // BM * G = 256 rows per workgroup
-  pp.nqb = (s->S + (1 << pp.bm_shift) - 1) >> pp.bm_shift;
+  pp.bm = 256 / pp.G;  // query positions per workgroup: G * BM <= 256 rows
+  pp.nqb = (s->S + pp.bm - 1) / pp.bm;
   // The kernel takes row maxima before applying the multiplier, so it needs a positive one: a
   // negative scale runs as -q with |scale| (negating bf16 is exact), a zero scale as q = 0 (every
   // score exactly 0, uniform weights over the visible keys).

@@ -242,7 +242,8 @@ uint64_t gqa_kv_bytes_per_token(uint32_t layers, uint32_t kv_heads, uint32_t hea
  * Layout (device memory, 16-byte aligned): q [B, Hq, S, d], k and v [B, Hkv, S, d] (bf16), out
  * [B, Hq, S, d] (bf16 rounded to nearest even, or f32).  Each K/V tile is read once per workgroup and
  * serves the G query heads of its group; nothing is expanded to Hq heads.  Supported: d in {64, 128},
- * G a power of two up to 32.  No workspace.  Enqueued on `stream`; asynchronous.
+ * any G = Hq / Hkv up to 64 (a workgroup takes floor(256 / G) positions of all G heads).  No workspace.
+ * Enqueued on `stream`; asynchronous.
  */
 typedef struct {
   int32_t B, Hq, Hkv, S, d;

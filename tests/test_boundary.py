@@ -311,3 +311,22 @@ def test_binding_refuses_to_import_without_the_library(tmp_path):
                        timeout=300)
     assert r.returncode == 3, (r.returncode, r.stdout, r.stderr)
     assert "libgqa.so is missing" in r.stdout and "build.py" in r.stdout
+
+
+def _pshape(**kw):
+    base = dict(B=1, Hq=32, Hkv=8, S=1024, d=128, dtype=gqa.BF16, out_dtype=gqa.BF16, causal=1)
+    base.update(kw)
+    return gqa.PrefillShape(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), 0), (dict(Hq=40), 0), (dict(Hq=24, Hkv=8), 0), (dict(Hq=7, Hkv=1), 0),
+    (dict(Hq=64, Hkv=1), 0), (dict(Hq=128, Hkv=2, d=64), 0), (dict(out_dtype=gqa.F32, causal=0), 0),
+    (dict(Hq=65, Hkv=1), 2),                # group larger than 64
+    (dict(Hq=36), 1),                       # Hq not a multiple of Hkv
+    (dict(d=96), 2), (dict(dtype=gqa.F32), 2), (dict(out_dtype=gqa.FP8_E4M3), 2),
+    (dict(causal=2), 1), (dict(S=0), 1), (dict(dtype=9), 1),
+    (dict(S=1 << 23, d=128), 2),            # K/V slice beyond 32-bit byte offsets
+])
+def test_prefill_shape_check(kw, code):
+    assert gqa.lib.gqa_prefill_shape_check(ctypes.byref(_pshape(**kw))) == code

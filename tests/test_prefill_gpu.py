@@ -3,6 +3,8 @@
 bf16 inputs with fp32 accumulation; the weights are rounded to bf16 before P V, as in decode, so the
 bf16 gates apply (1e-2 absolute, and relative to the reference's scale).
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -32,6 +34,12 @@ SMALL = [
     (1, 16, 1, 33, 64),      # G = 16
     (1, 32, 1, 60, 128),     # G = 32: a 16-row tile spans two heads
     (1, 8, 8, 1, 128),       # a one-token prompt
+    (1, 40, 8, 90, 128),     # G = 5: 51 positions per workgroup, one padding row
+    (2, 12, 4, 100, 64),     # G = 3: 85 positions, one padding row
+    (1, 7, 1, 300, 128),     # G = 7: 36 positions, four padding rows
+    (1, 24, 1, 70, 128),     # G = 24: 10 positions, sixteen padding rows (one whole tile)
+    (1, 48, 1, 37, 64),      # G = 48: 5 positions, a wave of padding rows
+    (1, 64, 1, 20, 128),     # G = 64: 4 positions
 ]
 
 
@@ -66,23 +74,33 @@ def test_prefill_is_deterministic():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["prefill-8b", "prefill-70b"])
+@pytest.mark.parametrize("name", ["prefill-8b", "prefill-40b", "prefill-70b"])
 def test_prefill_workload_parity(name):
-    """Full-size prefill workloads; the oracle checks sampled (b, h, i) rows: first and last
-    positions, both ends of every query block boundary sampled, and random rows."""
+    """Full-size prefill workloads against the oracle (rows cut over the host's CPUs).  prefill-8b
+    and prefill-40b: every (b, h, i) row.  prefill-70b (1.1 TFLOP of fp64 oracle work in all): every
+    position of the first and the last query group (the 8 heads of KV heads 0 and 7, a quarter of
+    the rows) and 2000 random rows of the other groups."""
     w = workloads.PREFILL_WORKLOADS[name]
     say(f"prefill workload {name}: {w.name}")
     case = workloads.make_prefill(name)
     got = run(case).cpu()
-    rng = np.random.default_rng(93)
-    BM = 256 // w.G
-    rows = {(0, 0, 0), (w.B - 1, w.Hq - 1, w.S - 1), (0, w.G - 1, BM - 1), (0, w.G, BM), (w.B - 1, 1, w.S - 2)}
-    while len(rows) < 40:
-        rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.S))))
-    rows = sorted(rows)
-    want = ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", True, rows=rows)
-    sel = torch.stack([got[b, h, i] for b, h, i in rows])
-    compare(sel, want, "bf16", f"{name} {len(rows)} rows")
+    t0 = time.perf_counter()
+    if name != "prefill-70b":
+        want = ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", True, rows="all",
+                           threads=ref.host_threads())
+        label = f"{name} all {w.B * w.Hq * w.S} rows"
+    else:
+        rng = np.random.default_rng(93)
+        heads = list(range(w.G)) + list(range(w.Hq - w.G, w.Hq))
+        rows = [(b, h, i) for b in range(w.B) for h in heads for i in range(w.S)]
+        rows += [(int(rng.integers(w.B)), int(rng.integers(w.G, w.Hq - w.G)), int(rng.integers(w.S)))
+                 for _ in range(2000)]
+        want = ref.prefill(case["q"], case["k"], case["v"], case["scale"], "bf16", True, rows=rows,
+                           threads=ref.host_threads())
+        got = torch.stack([got[b, h, i] for b, h, i in rows])
+        label = f"{name} {len(rows)} rows"
+    say(f"  oracle: {time.perf_counter() - t0:.1f} s on {ref.host_threads()} threads")
+    compare(got, want, "bf16", label)
 
 
 @pytest.mark.parametrize("scale", [-0.11, -1.0, 0.0, -0.0])
@@ -121,7 +139,21 @@ def _random_prefill(n, seed):
     return out
 
 
-@pytest.mark.parametrize("cfg", _random_prefill(12, 13), ids=lambda c: "B{}Hq{}Hkv{}S{}d{}-causal{}".format(*c))
+def _random_prefill_any_group(n, seed):
+    """Group sizes 1..64 that need not divide 256 (padding rows in every workgroup)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hkv = int(rng.choice([1, 2, 3]))
+        G = int(rng.integers(1, 65))
+        d = int(rng.choice([64, 128]))
+        S = int(rng.integers(1, 300))
+        out.append((int(rng.integers(1, 3)), G * Hkv, Hkv, S, d, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_prefill(12, 13) + _random_prefill_any_group(12, 14),
+                         ids=lambda c: "B{}Hq{}Hkv{}S{}d{}-causal{}".format(*c))
 def test_prefill_random_shapes(cfg):
     """Seeded random prompt shapes (every supported group size, ragged query and key blocks)."""
     B, Hq, Hkv, S, d, causal = cfg

@@ -179,6 +179,8 @@ class PrefillWorkload:
 PREFILL_WORKLOADS = {
     "prefill-8b": PrefillWorkload("prefill llama3-8b-layer B2 Hq32 Hkv8 d128 S4096", 2, 32, 8, 128, 4096, seed=1101),
     "prefill-70b": PrefillWorkload("prefill llama-70b-layer B1 Hq64 Hkv8 d128 S8192", 1, 64, 8, 128, 8192, seed=1102),
+    # 40 query heads on 8 KV heads: a group of 5, which does not divide a workgroup's 256 rows
+    "prefill-40b": PrefillWorkload("prefill 40b-class-layer B1 Hq40 Hkv8 d128 S4096", 1, 40, 8, 128, 4096, seed=1103),
 }
 
 
