@@ -31,9 +31,11 @@ sys.path.insert(0, ROOT)
 METRIC = "KV GB/s and % HBM roofline for GQA decode (Hq=64,Hkv=8,d=128,bf16)"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of an MI355X
-# rocprofv3 counter summaries of the 70B-shaped layer, keyed by page size (0 = dense cache)
-TRAFFIC_SUMMARY = {0: os.path.join(ROOT, "profiles", "gqa_decode_llama70b_traffic.md"),
-                   16: os.path.join(ROOT, "profiles", "gqa_decode_paged16_llama70b_traffic.md")}
+# rocprofv3 counter summaries, keyed by (workload, page size) (page size 0 = dense cache)
+TRAFFIC_SUMMARY = {(3, 0): os.path.join(ROOT, "profiles", "gqa_decode_llama70b_traffic.md"),
+                   (3, 16): os.path.join(ROOT, "profiles", "gqa_decode_paged16_llama70b_traffic.md"),
+                   (5, 0): os.path.join(ROOT, "profiles", "gqa_decode_long_fp8_trace_traffic_counters.md"),
+                   (2, 0): os.path.join(ROOT, "profiles", "gqa_decode_llama3_8b_trace_traffic_counters.md")}
 KERNEL_SOURCES = [os.path.join(ROOT, "grouped_query_attention_04_amd", "csrc", f)
                   for f in ("gqa_device.h", "gqa_kernels.h", "gqa_api.hip")]
 
@@ -53,8 +55,8 @@ def kernel_source_hash():
 def recorded_traffic(wid, workgroups, paged=0):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on this
     workload, layout and launch configuration with the kernel sources as they are now; else None."""
-    path = TRAFFIC_SUMMARY.get(paged)
-    if wid != 3 or workgroups != 0 or path is None or not os.path.exists(path):
+    path = TRAFFIC_SUMMARY.get((wid, paged))
+    if workgroups != 0 or path is None or not os.path.exists(path):
         return None
     text = open(path).read()
     src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
