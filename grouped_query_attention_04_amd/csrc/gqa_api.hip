@@ -198,21 +198,25 @@ std::mutex static_scratch_mu;
 void* static_scratch_ptr[kMaxDevices];  // guarded by static_scratch_mu; set once per device
 
 // The device address of this GPU's scratch, set up on the device's first call: the address looked
-// up once, and the workspace initialised (header tag, counters cleared) by a kernel on `stream`, so
-// the decode enqueued after it on the same stream finds it ready.  nullptr on a HIP error.
-void* static_scratch(hipStream_t stream, int* dev_out) {
+// up, and the workspace initialised (header tag, counters cleared) by a kernel on `stream`, so the
+// decode enqueued after it on the same stream finds it ready.  An initialisation enqueued while
+// `stream` is being captured into a graph runs only when the graph does, so the device is marked
+// ready only by one enqueued outside a capture (until then every call enqueues it again).  nullptr
+// on a HIP error.
+void* static_scratch(hipStream_t stream) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  *dev_out = dev;
   std::lock_guard<std::mutex> lock(static_scratch_mu);
   if (static_scratch_ptr[dev]) return static_scratch_ptr[dev];
   void* ptr = nullptr;
   if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &capture) != hipSuccess) return nullptr;
   const int n = (int)((kHeaderBytes + kMaxUnits * sizeof(uint32_t)) / sizeof(uint32_t));
   hipLaunchKernelGGL(gqa::init_workspace_kernel, dim3((n + 255) / 256), dim3(256), 0, stream,
                      static_cast<uint32_t*>(ptr), n);
   if (hipGetLastError() != hipSuccess) return nullptr;
-  static_scratch_ptr[dev] = ptr;
+  if (capture == hipStreamCaptureStatusNone) static_scratch_ptr[dev] = ptr;
   return ptr;
 }
 
@@ -300,8 +304,7 @@ gqa_status_t gqa_decode_static(const void* q, const void* k_cache, const void* v
   const gqa_status_t st = gqa_shape_check(s);
   if (st != GQA_OK) return st;
   if (plan(s).total > (size_t)GQA_STATIC_SCRATCH_BYTES) return GQA_ERR_WORKSPACE;
-  int dev = -1;
-  void* ws = static_scratch((hipStream_t)stream, &dev);
+  void* ws = static_scratch((hipStream_t)stream);
   if (!ws) return GQA_ERR_HIP;
   return gqa_decode(q, k_cache, v_cache, seq_lens, scale, out, s, ws, GQA_STATIC_SCRATCH_BYTES, stream);
 }

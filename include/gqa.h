@@ -110,7 +110,9 @@ gqa_status_t gqa_decode(const void* q, const void* k_cache, const void* v_cache,
  * checks and kernels as gqa_decode, but the workspace is a fixed array of GQA_STATIC_SCRATCH_BYTES
  * inside the library, one per GPU, held until the process ends; no call allocates or frees memory.
  * The first call on a device looks the array up and initialises it with a small kernel on `stream`;
- * later calls find its counters back at zero.  Shapes whose workspace (gqa_decode_workspace_bytes)
+ * later calls find its counters back at zero.  (A first call made while `stream` is being captured
+ * into a graph puts the initialisation into the graph, and the next call outside a capture
+ * initialises the array again.)  Shapes whose workspace (gqa_decode_workspace_bytes)
  * exceeds GQA_STATIC_SCRATCH_BYTES return GQA_ERR_WORKSPACE before any HIP call; a HIP error while
  * setting the array up returns GQA_ERR_HIP.  All calls on one GPU share its array, so calls that
  * overlap in time on one GPU (on different streams or from several threads without ordering) race

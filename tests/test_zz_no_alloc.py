@@ -29,6 +29,46 @@ def _static(case, out_dtype, wg=0):
     return rc, out, d
 
 
+def _static_call(d, case, out, shape):
+    return gqa.lib.gqa_decode_static(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
+                                     d["seq_lens"].data_ptr(), float(case["scale"]), out.data_ptr(),
+                                     ctypes.byref(shape), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+
+def test_static_scratch_under_graph_capture():
+    """A call captured into a graph (possibly the device's first, whose set-up then goes into the
+    graph too), an eager call made before the graph is ever replayed, and three replays with eager
+    calls between them: every result equals gqa_decode's, bitwise."""
+    say("static scratch under graph capture")
+    case = workloads.make_case(4, 32, 8, 128, 1500, "bf16", "bf16", seq_range=(1, 1500), seed=203)
+    other = workloads.make_case(2, 16, 2, 128, 900, "bf16", "fp8_e4m3", seq_lens=(900, 17), seed=204)
+    d = {n: case[n].to(DEV) for n in ("q", "k", "v", "seq_lens")}
+    d2 = {n: other[n].to(DEV) for n in ("q", "k", "v", "seq_lens")}
+    shape = gqa.make_shape(4, 32, 8, 1500, 128, gqa.BF16, gqa.BF16, gqa.BF16)
+    shape2 = gqa.make_shape(2, 16, 2, 900, 128, gqa.BF16, gqa.FP8_E4M3, gqa.F32)
+    want = gqa.decode(d["q"], d["k"], d["v"], d["seq_lens"], case["scale"])
+    want2 = gqa.decode(d2["q"], d2["k"], d2["v"], d2["seq_lens"], other["scale"], out_dtype=torch.float32)
+    out = torch.full_like(want, float("nan"))
+    out2 = torch.full_like(want2, float("nan"))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        assert _static_call(d, case, out, shape) == 0
+    torch.cuda.synchronize()
+    assert _static_call(d2, other, out2, shape2) == 0      # eager, before any replay
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.uint8), want2.view(torch.uint8)), "eager call before the first replay"
+    for rep in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.uint8), want.view(torch.uint8)), f"replay {rep}"
+        out2.fill_(float("nan"))
+        assert _static_call(d2, other, out2, shape2) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(out2.view(torch.uint8), want2.view(torch.uint8)), f"eager call after replay {rep}"
+
+
 def test_static_scratch_decode_matches_the_workspace_decode():
     cases = [
         # a large call first (shared segments merged through the static array), then a smaller one
