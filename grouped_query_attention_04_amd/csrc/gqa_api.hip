@@ -29,16 +29,40 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int elt_bytes(int dt) { return dt == GQA_F32 ? 4 : dt == GQA_BF16 ? 2 : 1; }
 
-// The library's workgroup count.  Every segment that several workgroups share is merged at the end
-// by the one that finishes it last, in rounds of partial-result loads whose size grows with the
-// group; above 16 query heads per KV head a round takes four pieces.  With few (batch, KV head)
-// segments, 256 workgroups then cut each into 32 or more pieces whose merge outlasts the streaming
-// (B8 Hq32 Hkv1 L4096: 28.8 us at 256 workgroups, 19.9 us at 64), so there the count is capped at
+// Query-head split of the matrix-core kernels.  A group of more than 16 query heads takes two or
+// four 16-row query tiles per workgroup, and with few (batch, KV head) pairs such a launch is bound
+// by latency, not bytes: each tile's products, the per-piece epilogue and the merge all grow with
+// the group while the cache is small.  There each group is cut into hs sub-groups of at most 16
+// heads, and every sub-group is a segment of its own (segment head j reads cache head j / hs): hs
+// workgroups read each cache tile, each for G / hs query heads.  The hs segments of a cache head are
+// adjacent in the tile space, so with 8 or more workgroups per segment the workgroups that read the
+// same tiles run at the same time on the same XCD and its L2 serves the repeated reads (B8 Hq64 Hkv1
+// L4096: HBM reads 1.2x the cache bytes, 31.0 -> 16.6 us).  hs is the smallest of 2, 3 and 4 that
+// divides G into sub-groups of at most 16 (none for other group sizes), used when the split leaves
+// at most 32 segments, or 64 for groups above 32 (whose unsplit kernel carries four query tiles):
+// B16 Hq64 Hkv1 L4096 32.0 -> 24.7 us at 64 segments, while B32 Hq32 Hkv1 L4096 (64 segments)
+// runs 22.7 us unsplit and 27.8 split.
+int plan_split(const gqa_shape_t* s) {
+  if (s->kv_dtype == GQA_F32) return 1;
+  const int G = s->Hq / s->Hkv;
+  if (G <= 16) return 1;
+  const long long max_segments = G > 32 ? 64 : 32;
+  for (int hs = 2; hs <= 4; ++hs)
+    if (G % hs == 0 && G / hs <= 16) return (long long)s->B * s->Hkv * hs <= max_segments ? hs : 1;
+  return 1;
+}
+
+// The library's workgroup count, for segments of G query heads on Hkv segment heads per batch entry
+// (after the split).  Every segment that several workgroups share is merged at the end by the one
+// that finishes it last, in rounds of partial-result loads whose size grows with the group; above
+// 16 query heads per segment a round takes four pieces.  With few segments, 256 workgroups then cut
+// each into 32 or more pieces whose merge outlasts the streaming (measured on B8 Hq32 Hkv1 L4096
+// before the split: 28.8 us at 256 workgroups, 19.9 us at 64), so there the count is capped at
 // eight pieces per segment on average, and at least 64 workgroups.
-int plan_workgroups(const gqa_shape_t* s) {
+int plan_workgroups(const gqa_shape_t* s, int G, int Hkv) {
   if (s->num_workgroups > 0) return s->num_workgroups;
-  if (s->Hq / s->Hkv > 16) {
-    const long long cap = 8ll * s->B * s->Hkv;
+  if (G > 16) {
+    const long long cap = 8ll * s->B * Hkv;
     return (int)std::max(64ll, std::min((long long)kDefaultWorkgroups, cap));
   }
   return kDefaultWorkgroups;
@@ -53,19 +77,21 @@ constexpr size_t kMaxUnits = size_t(1) << 18;
 constexpr size_t kHeaderBytes = gqa::kWorkspaceHeaderWords * sizeof(uint32_t);
 
 struct Layout {
+  int split;  // query-head split hs
   int workgroups;
   size_t counters_off, ml_off, o_off, total;
 };
 
 Layout plan(const gqa_shape_t* s) {
   Layout lo;
-  lo.workgroups = plan_workgroups(s);
+  lo.split = plan_split(s);
+  const int G = s->Hq / s->Hkv / lo.split;  // query heads per segment
+  lo.workgroups = plan_workgroups(s, G, s->Hkv * lo.split);
   const size_t slots = (size_t)lo.workgroups * 2;  // two per workgroup
-  const size_t G = (size_t)(s->Hq / s->Hkv);
   lo.counters_off = kHeaderBytes;
   lo.ml_off = kHeaderBytes + kMaxUnits * sizeof(uint32_t);
-  lo.o_off = lo.ml_off + align_up(slots * G * 2 * sizeof(float));
-  lo.total = lo.o_off + align_up(slots * G * (size_t)s->d * sizeof(float));
+  lo.o_off = lo.ml_off + align_up(slots * (size_t)G * 2 * sizeof(float));
+  lo.total = lo.o_off + align_up(slots * (size_t)G * (size_t)s->d * sizeof(float));
   return lo;
 }
 
@@ -132,9 +158,10 @@ gqa::Params base_params(const void* q, const void* k, const void* v, const int32
   prm.part_o = reinterpret_cast<float*>(ws + lo.o_off);
   prm.B = s->B;
   prm.Hq = s->Hq;
-  prm.Hkv = s->Hkv;
+  prm.Hkv = s->Hkv * lo.split;
   prm.L = s->L;
-  prm.G = s->Hq / s->Hkv;
+  prm.G = s->Hq / prm.Hkv;
+  prm.hs = lo.split;
   prm.W = lo.workgroups;
   prm.qk_scale = (float)((double)scale * (double)s->k_descale * 1.4426950408889634);
   prm.v_descale = s->v_descale;

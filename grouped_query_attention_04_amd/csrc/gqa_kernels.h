@@ -35,7 +35,11 @@ struct Params {
   float* part_ml;      // [W][2][G][2] their (max, sum), base-2 domain
   uint32_t* counters;  // [B*Hkv] finished-piece counters, zero between calls
   uint32_t* header;    // workspace header: tag words 0-1, error count word 2
+  // Hkv and G describe the kernel's segments: with a query-head split of hs, every KV head of the
+  // cache serves hs consecutive segment heads j (cache head j / hs), each with G = Hq / Hkv of its
+  // query heads; hs = 1 is the plain layout.
   int B, Hq, Hkv, L, G;
+  int hs;
   int W;            // workgroups launched
   float qk_scale;   // scale * k_descale * log2(e)
   float v_descale;  // applied to the normalised output
@@ -515,7 +519,9 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
         }
       }
     }
-    const size_t head = PAGED ? 0 : ((size_t)pc.b * p.Hkv + pc.j) * (size_t)p.L * ROWB;
+    const int hkv = p.Hkv / p.hs;       // KV heads of the cache
+    const int jc = uniform(pc.j / p.hs);  // the cache's KV head of this segment
+    const size_t head = PAGED ? 0 : ((size_t)pc.b * hkv + jc) * (size_t)p.L * ROWB;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const char*>(p.k) + head, (uint32_t)n * ROWB);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const char*>(p.v) + head, (uint32_t)n * ROWB);
     const int mine = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;  // piece tiles w, w+NW, ...
@@ -524,10 +530,13 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
     // that owns ap's tile loads the rows' bf16 source now, D / 64 elements of each row per lane;
     // when it computes that tile it converts them to the cache format (spread over all lanes, as
     // the fp8 conversion is long), gathers the 16-byte chunks each lane holds of row ap through
-    // LDS, puts them in place of the loaded ones and writes them to the cache.
+    // LDS, puts them in place of the loaded ones and writes them to the cache.  Under a query-head
+    // split the hs segments of one cache head each patch their own copy of the tile, and only the
+    // first (j % hs == 0) writes the rows to the cache.
     constexpr int EPL = D / 64;         // elements of each new row per lane
     constexpr int CPRB = ROWB / 16;     // 16-byte cache chunks per row
     int ap_it = -1, ap_row = 0;         // the wave's iteration of ap's tile, and ap's row in it
+    const bool ap_store = pc.j % p.hs == 0;  // this segment writes the new rows to the cache
     uint32_t kw = 0, vw = 0;            // this lane's source elements (bf16 bits) of the new rows
     if constexpr (APPEND) {
       const int raw = *(const GQA_CONST int32_t*)(uintptr_t)(p.seq_lens + pc.b);  // scalar load
@@ -536,7 +545,7 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
       if (ap >= 0 && ap < p.L && rel >= 0 && rel < ntiles && rel % NW == w) {
         ap_it = rel / NW;
         ap_row = ap % TILE;
-        const size_t row = ((size_t)pc.b * p.Hkv + pc.j) * D;
+        const size_t row = ((size_t)pc.b * hkv + jc) * D;
         if constexpr (EPL == 2) {
           kw = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.k_new) + row)[l];
           vw = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.v_new) + row)[l];
@@ -583,7 +592,7 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
           const int lpage = (int)(t0 >> p.block_shift);  // logical page of the tile
           const int rows = min(1 << p.block_shift, n - (lpage << p.block_shift));
           const uint32_t bytes = (uint32_t)page < (uint32_t)p.num_blocks ? (uint32_t)rows * ROWB : 0u;
-          const size_t pbase = (((size_t)page * p.Hkv + pc.j) << p.block_shift) * ROWB;
+          const size_t pbase = (((size_t)page * hkv + jc) << p.block_shift) * ROWB;
           tk = make_rsrc(static_cast<const char*>(p.k) + pbase, bytes);
           tv = make_rsrc(static_cast<const char*>(p.v) + pbase, bytes);
           t0 &= (1u << p.block_shift) - 1;  // position within the page
@@ -613,7 +622,7 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
           if constexpr (PAGED) {
             const int page = R.page;  // this tile's page (the entry for the set's next tile comes below)
             ok = (uint32_t)page < (uint32_t)p.num_blocks;
-            const size_t pbase = (((size_t)page * p.Hkv + pc.j) << p.block_shift) * ROWB;
+            const size_t pbase = (((size_t)page * hkv + jc) << p.block_shift) * ROWB;
             const uint32_t bytes = ok ? (uint32_t)ROWB << p.block_shift : 0u;
             tk = make_rsrc(static_cast<const char*>(p.k) + pbase, bytes);
             tv = make_rsrc(static_cast<const char*>(p.v) + pbase, bytes);
@@ -654,7 +663,7 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
               for (int x = 0; x < NK; ++x) {
                 const u32x4_t c = *reinterpret_cast<const u32x4_t*>(as + x * 64 + q * 16);
                 R.k[x] = c;
-                __builtin_amdgcn_raw_buffer_store_b128(c, tk, (base + ap_row) * ROWB + x * 64 + q * 16, 0, 0);
+                if (ap_store) __builtin_amdgcn_raw_buffer_store_b128(c, tk, (base + ap_row) * ROWB + x * 64 + q * 16, 0, 0);
               }
             }
             const int lv = (ap_row * CPRB) % 64, xv = ap_row * CPRB / 64;
@@ -663,7 +672,7 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
 #pragma unroll
               for (int x = 0; x < NV; ++x)
                 if (x == xv) R.v[x] = c;
-              __builtin_amdgcn_raw_buffer_store_b128(c, tv, base * ROWB + (xv * 64 + l) * 16, 0, 0);
+              if (ap_store) __builtin_amdgcn_raw_buffer_store_b128(c, tv, base * ROWB + (xv * 64 + l) * 16, 0, 0);
             }
           }
         }

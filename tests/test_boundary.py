@@ -94,18 +94,51 @@ def test_workspace_grows_with_workgroups_and_is_aligned():
     assert gqa.workspace_bytes(_shape(L=4096)) == gqa.workspace_bytes(_shape(L=4096, num_workgroups=256))
 
 
+def _ws_bytes(workgroups, rows, d):
+    """The library's workspace for `workgroups` workgroups whose segments carry `rows` query rows:
+    256-byte header, fixed counter area, then two published-piece slots per workgroup of (m, l) and d
+    floats per row, each region 256-byte aligned."""
+    up = lambda x: -(-x // 256) * 256
+    slots = 2 * workgroups
+    return 256 + (1 << 20) + up(slots * rows * 2 * 4) + up(slots * rows * d * 4)
+
+
 def test_default_workgroup_count():
-    """256 workgroups, except for groups above 16 query heads: at most eight pieces per (batch, KV
-    head) segment on average, and at least 64 workgroups (the workspace holds two slots each)."""
+    """256 workgroups, except for segments of more than 16 query heads: at most eight pieces per
+    segment on average, and at least 64 workgroups."""
     def same(kw, wg):
         return gqa.workspace_bytes(_shape(**kw)) == gqa.workspace_bytes(_shape(num_workgroups=wg, **kw))
     bf = dict(q_dtype=gqa.BF16, kv_dtype=gqa.BF16, L=4096, d=128)
     assert same(dict(B=8, Hq=32, Hkv=8, **bf), 256)
     assert same(dict(B=8, Hq=16, Hkv=1, **bf), 256)      # G = 16: unchanged
-    assert same(dict(B=8, Hq=32, Hkv=1, **bf), 64)       # G = 32, 8 segments
-    assert same(dict(B=1, Hq=32, Hkv=1, **bf), 64)       # the floor
+    assert same(dict(B=17, Hq=32, Hkv=1, **bf), 136)     # G = 32 on 17 segments (no query-head split)
+    assert same(dict(B=2, Hq=34, Hkv=1, **bf), 64)       # the floor (34 splits into no sub-groups <= 16)
     assert same(dict(B=20, Hq=64, Hkv=2, **bf), 256)     # 40 segments: 320 capped at 256
-    assert same(dict(B=12, Hq=32, Hkv=1, **bf), 96)
+    assert same(dict(B=12, Hq=34, Hkv=1, **bf), 96)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,kv,wg,workgroups,rows", [
+    (8, 32, 1, "bf16", 0, 256, 16),     # G = 32, 8 segments: split in two, 16 segments of 16 heads
+    (16, 32, 1, "bf16", 0, 256, 16),    # 32 segments after the split: still split
+    (17, 32, 1, "bf16", 0, 136, 32),    # 34 would be too many: G = 32 kept, workgroups capped
+    (1, 32, 1, "bf16", 0, 256, 16),
+    (8, 64, 1, "bf16", 0, 256, 16),     # G = 64 in four
+    (16, 64, 1, "fp8", 0, 256, 16),     # 64 segments: the limit above 32 heads per group
+    (17, 64, 1, "bf16", 0, 136, 64),
+    (20, 64, 2, "bf16", 0, 256, 32),    # G = 32 on 80 segments after a split: not split
+    (8, 48, 1, "bf16", 0, 256, 16),     # G = 48 in three
+    (4, 40, 1, "bf16", 0, 256, 10),     # G = 40 in four sub-groups of 10
+    (2, 34, 1, "bf16", 0, 64, 34),      # G = 34: no sub-group size <= 16 from 2, 3 or 4
+    (2, 32, 1, "f32", 0, 64, 32),       # the vector path is never split
+    (8, 64, 1, "bf16", 37, 37, 16),     # a caller's workgroup count keeps the split
+])
+def test_query_head_split_plan(B, Hq, Hkv, kv, wg, workgroups, rows):
+    """Groups of more than 16 query heads with few (batch, KV head) pairs run as sub-groups of at
+    most 16 heads (hs = 2, 3 or 4 of them), when that leaves at most 32 segments (64 for groups
+    above 32); the workspace, two slots per workgroup sized by the segment's rows, shows the plan."""
+    dt = {"bf16": (gqa.BF16, gqa.BF16), "fp8": (gqa.BF16, gqa.FP8_E4M3), "f32": (gqa.F32, gqa.F32)}[kv]
+    s = _shape(B=B, Hq=Hq, Hkv=Hkv, L=4096, d=128, q_dtype=dt[0], kv_dtype=dt[1], num_workgroups=wg)
+    assert gqa.workspace_bytes(s) == _ws_bytes(workgroups, rows, 128)
 
 
 def test_decode_rejects_before_any_hip_call():

@@ -61,7 +61,7 @@ SEQ = [1, 16, 17, 320, 0, 321, 150, 255, 33, 64]
 @pytest.mark.parametrize("paged", [False, True])
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (64, 2)])
+@pytest.mark.parametrize("Hq,Hkv", [(16, 2), (64, 2), (64, 1)])   # (64, 1): split into four sub-groups
 @pytest.mark.parametrize("wg", [0, 7])
 def test_fused_matches_oracle(paged, kv, d, Hq, Hkv, wg):
     say(f"fused append+decode paged={paged} kv={kv} d={d} Hq={Hq} Hkv={Hkv} workgroups={wg}")

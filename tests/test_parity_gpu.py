@@ -539,6 +539,43 @@ def test_random_shapes(cfg):
             assert (got[b] == 0).all()
 
 
+# ------------------------------------------------------------------------------ query-head split
+# Shapes on both sides of the library's query-head split (groups above 16 heads run as sub-groups of
+# at most 16 when that leaves at most 32 segments, 64 for groups above 32), against the oracle.
+SPLIT = [
+    (16, 32, 1, 128, 700, "bf16", 0),     # 32 segments after the split: split
+    (17, 32, 1, 128, 700, "bf16", 0),     # 34: not split
+    (16, 64, 1, 128, 600, "fp8_e4m3", 0),  # 64: split in four
+    (17, 64, 1, 64, 600, "bf16", 0),      # 68: not split
+    (8, 48, 1, 128, 500, "bf16", 37),     # G = 48 in three, odd workgroup count
+    (4, 40, 1, 128, 900, "fp8_e4m3", 0),  # G = 40 in four sub-groups of 10
+    (3, 34, 1, 64, 400, "bf16", 0),       # G = 34: never split
+    (2, 128, 2, 128, 1100, "bf16", 4096),  # G = 64 on two KV heads, more workgroups than tiles
+]
+
+
+@pytest.mark.parametrize("cfg", SPLIT, ids=lambda c: "B{}Hq{}Hkv{}d{}L{}-{}-wg{}".format(*c))
+def test_query_head_split_boundary(cfg):
+    B, Hq, Hkv, d, L, kd, wg = cfg
+    say(f"query-head split shape {cfg}")
+    rng = np.random.default_rng(B * 1000 + Hq)
+    sl = rng.integers(0, L + 1, size=B)
+    sl[0], sl[-1] = L, 1
+    case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", kd, seq_lens=tuple(int(x) for x in sl),
+                               seed=B * 7 + Hq)
+    got = run(case, out_dtype="f32", workgroups=wg)
+    compare(got, oracle_full(case), kd, f"split {cfg}")
+    # the same shape through the dense and the paged entry points agrees bit for bit
+    bs = 16
+    pg = workloads.paginate(case, bs, seed=3)
+    d_ = to_dev(case)
+    paged = gqa.decode_paged(d_["q"], pg["k_pages"].to(DEV), pg["v_pages"].to(DEV), pg["block_table"].to(DEV),
+                             d_["seq_lens"], case["scale"], out_dtype=torch.float32,
+                             num_workgroups=wg)
+    torch.cuda.synchronize()
+    assert torch.equal(paged, got)
+
+
 # ------------------------------------------------------------------------------ large batches
 def _serving_lengths(B, L, seed):
     """A serving-like mix of sequence lengths: empty, single-token, ragged and full-length ones."""
