@@ -64,9 +64,14 @@ typedef struct {
   int32_t q_dtype, kv_dtype, out_dtype; /* gqa_dtype_t values */
   float k_descale, v_descale;           /* 1.0 for f32 and bf16 caches */
   int32_t num_workgroups; /* workgroups that split the cache: 0 = library's choice, else
-                             1..65536.  The choice is 256, except with more than 16 query heads
-                             per KV head: min(256, max(64, 8 * B * Hkv)).  Results do not depend
-                             on it beyond rounding. */
+                             1..65536.  The choice is 256, except for groups of more than 16 query
+                             heads that are not split into sub-groups (below): min(256, max(64,
+                             8 * B * Hkv)).  Results do not depend on it beyond rounding.
+                             Bf16 and fp8 caches: a group of more than 16 query heads with few
+                             (batch, KV head) pairs (at most 32 sub-group segments, 64 above 32
+                             heads) runs as 2, 3 or 4 sub-groups of at most 16 heads, each of
+                             which reads its KV head's cache; the choice depends on the
+                             shape only. */
 } gqa_shape_t;
 
 /* Validates a shape (dimensions, divisibility, dtypes, workgroup count, 32-bit offsets).
