@@ -31,9 +31,9 @@ struct Params {
   const void* v;
   const int32_t* seq_lens;
   void* out;
-  float* part_o;       // [W][2][G][D] unnormalised outputs of published pieces
+  float* part_o;       // [W][2][G][D] unnormalised outputs of published pieces (G, Hkv: of the segments)
   float* part_ml;      // [W][2][G][2] their (max, sum), base-2 domain
-  uint32_t* counters;  // [B*Hkv] finished-piece counters, zero between calls
+  uint32_t* counters;  // [B*Hkv] finished-piece counters, one per segment, zero between calls
   uint32_t* header;    // workspace header: tag words 0-1, error count word 2
   // Hkv and G describe the kernel's segments: with a query-head split of hs, every KV head of the
   // cache serves hs consecutive segment heads j (cache head j / hs), each with G = Hq / Hkv of its
@@ -43,11 +43,11 @@ struct Params {
   int W;            // workgroups launched
   float qk_scale;   // scale * k_descale * log2(e)
   float v_descale;  // applied to the normalised output
-  // paged cache only: k and v are page pools [num_blocks][Hkv][block_size][D]; block_table is
+  // paged cache only: k and v are page pools [num_blocks][Hkv / hs][block_size][D]; block_table is
   // [B][max_blocks]; block_size = 1 << block_shift positions per page.
   const int32_t* block_table;
   int block_shift, max_blocks, num_blocks;
-  // fused append (decode_mfma_kernel with APPEND): the new rows k_new, v_new [B][Hkv][D] (bf16) go
+  // fused append (decode_mfma_kernel with APPEND): the new rows k_new, v_new [B][Hkv / hs][D] (bf16) go
   // to position seq_lens[b] - 1, in the cache format (fp8: code of x / enc_descale).
   const void* k_new;
   const void* v_new;
@@ -842,6 +842,7 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
       for (int idx = threadIdx.x; idx < GT * D; idx += NTH) qs[idx] = (idx / D < G) ? qg[idx] : 0.f;
     }
     __syncthreads();
+    // the host never splits the group on this path (hs = 1), so segment heads are cache heads
     const float* kh = reinterpret_cast<const float*>(p.k) + ((size_t)pc.b * p.Hkv + pc.j) * (size_t)p.L * D;
     const float* vh = reinterpret_cast<const float*>(p.v) + ((size_t)pc.b * p.Hkv + pc.j) * (size_t)p.L * D;
 
