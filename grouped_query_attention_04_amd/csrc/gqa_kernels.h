@@ -863,14 +863,19 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
 #pragma unroll
       for (int g = 0; g < GT; ++g) s[g] = 0.f;
       if (valid) {
+        // this lane's key row, eight 16-byte loads in flight at a time
         const float4* kr = reinterpret_cast<const float4*>(kh + (size_t)t * D);
-        for (int c4 = 0; c4 < D / 4; ++c4) {
-          const float4 kv = kr[c4];
+        for (int c0 = 0; c0 < D / 4; c0 += 8) {
+          float4 kv[8];
 #pragma unroll
-          for (int g = 0; g < GT; ++g) {
-            const float4 qv = *reinterpret_cast<const float4*>(qs + g * D + 4 * c4);
-            s[g] += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
-          }
+          for (int u = 0; u < 8; ++u) kv[u] = kr[c0 + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int g = 0; g < GT; ++g) {
+              const float4 qv = *reinterpret_cast<const float4*>(qs + g * D + 4 * (c0 + u));
+              s[g] += qv.x * kv[u].x + qv.y * kv[u].y + qv.z * kv[u].z + qv.w * kv[u].w;
+            }
         }
       }
 #pragma unroll
@@ -888,16 +893,25 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
         for (int x = 0; x < CPL; ++x) o[g][x] *= alpha;
         ps[g * TILE + l] = pw;
       }
+      // value rows in groups of eight, their loads in flight together (rows past the tile's last
+      // position are not read)
       const int cnt = min(TILE, n - t0);
-      for (int tt = 0; tt < cnt; ++tt) {
-        float vv[CPL];
+      for (int t8 = 0; t8 < cnt; t8 += 8) {
+        float vv[8][CPL];
 #pragma unroll
-        for (int x = 0; x < CPL; ++x) vv[x] = vh[(size_t)(t0 + tt) * D + 64 * x + l];
+        for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int g = 0; g < GT; ++g) {
-          const float pw = ps[g * TILE + tt];
+          for (int x = 0; x < CPL; ++x)
+            vv[u][x] = t8 + u < cnt ? vh[(size_t)(t0 + t8 + u) * D + 64 * x + l] : 0.f;
 #pragma unroll
-          for (int x = 0; x < CPL; ++x) o[g][x] += pw * vv[x];
+        for (int u = 0; u < 8; ++u) {
+          if (t8 + u >= cnt) break;
+#pragma unroll
+          for (int g = 0; g < GT; ++g) {
+            const float pw = ps[g * TILE + t8 + u];
+#pragma unroll
+            for (int x = 0; x < CPL; ++x) o[g][x] += pw * vv[u][x];
+          }
         }
       }
     }
