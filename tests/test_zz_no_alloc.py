@@ -74,6 +74,8 @@ def test_static_scratch_decode_matches_the_workspace_decode():
         # a large call first (shared segments merged through the static array), then a smaller one
         (workloads.make_case(6, 64, 8, 128, 3000, "bf16", "bf16", seq_range=(1, 3000), seed=201), "bf16", 0),
         (workloads.make_case(2, 16, 4, 128, 700, "bf16", "fp8_e4m3", seq_lens=(700, 233), seed=202), "f32", 37),
+        # 64 query heads on one KV head: run as four 16-head sub-groups, a workspace of their size
+        (workloads.make_case(4, 64, 1, 128, 800, "bf16", "bf16", seq_lens=(800, 1, 0, 513), seed=205), "bf16", 0),
     ]
     for i, (case, od, wg) in enumerate(cases):
         say(f"static scratch call {i}: B{case['B']} Hq{case['Hq']} Hkv{case['Hkv']} kv={case['kv_dtype']}")
