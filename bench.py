@@ -441,6 +441,9 @@ def main():
         "launch_us": lt,
         "end_to_end_us": e2e,
         "calibration_read_gbs": round(calib, 1),
+        # measured HBM bytes per launch over the algorithmic KV bytes: ~1.0 means the cache is read
+        # once for all query heads of a group; about G would mean the heads re-read it
+        "traffic_per_kv_byte": None if traffic is None else round(traffic / kv_bytes, 4),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample of the same workload")
