@@ -380,7 +380,10 @@ def test_one_workspace_serves_shapes_in_any_order():
 
 
 SOAK = [(3, 16, 4, 128, 2048, "bf16", 37), (2, 64, 8, 128, 3000, "fp8_e4m3", 256), (1, 8, 1, 64, 5000, "bf16", 300),
-        (7, 32, 1, 128, 900, "bf16", 0), (4, 24, 3, 128, 1500, "fp8_e4m3", 4096), (2, 8, 2, 128, 16, "bf16", 2)]
+        (7, 32, 1, 128, 900, "bf16", 0), (4, 24, 3, 128, 1500, "fp8_e4m3", 4096), (2, 8, 2, 128, 16, "bf16", 2),
+        # segments of two or three pieces, some merged by a workgroup that finds the others already
+        # counted (and then publishes nothing), some through the published partials: the same bits
+        (32, 64, 8, 128, 1024, "bf16", 0), (16, 32, 8, 128, 1500, "fp8_e4m3", 0)]
 
 
 @pytest.mark.parametrize("cfg", SOAK, ids=lambda c: "B{}Hq{}Hkv{}d{}L{}-{}-wg{}".format(*c))
