@@ -230,6 +230,22 @@ struct Piece {
   int slot;        // 0: the piece starts this workgroup's range, 1: it ends it
 };
 
+// One log-sum-exp combine step: (acc_m, acc_l, acc_o) absorbs a partial (m, l, o) whose weights are
+// relative to base-2 maximum m.  Written with explicit fused multiply-adds, so the rounding is the
+// same wherever it is inlined: the compiler's free choice of which product to fuse in x * a + y * b
+// differs between call sites, and the merges below must agree bit for bit whichever workgroup runs
+// them.
+__device__ __forceinline__ void lse_combine(float& acc_m, float& acc_l, f32x4_t& acc_o, float m, float l,
+                                            f32x4_t o) {
+  const float mn = fmaxf(acc_m, m);
+  const float a = __builtin_amdgcn_exp2f(acc_m - mn);
+  const float sc = __builtin_amdgcn_exp2f(m - mn);
+  acc_l = __builtin_fmaf(l, sc, acc_l * a);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc_o[c] = __builtin_fmaf(o[c], sc, acc_o[c] * a);
+  acc_m = mn;
+}
+
 // Log-sum-exp merge of a segment's npc published pieces (those of workgroups wfirst ..
 // wfirst + npc - 1, in that order) into the output rows.  Every thread carries the running (max,
 // sum, output) of NI items (4 consecutive columns of one query row each).  The pieces' partials
@@ -274,14 +290,8 @@ __device__ __forceinline__ void merge_pieces(const Params& p, OutT* out, int nit
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       if (i > 0 && uniform(i * NTH) >= nitems) break;  // not loaded: never stored either
-      const float m = __builtin_bit_cast(float, R.m[i]);
-      const float l = __builtin_bit_cast(float, R.l[i]);
-      const float mn = fmaxf(acc_m[i], m);
-      const float a = __builtin_amdgcn_exp2f(acc_m[i] - mn);
-      const float sc = __builtin_amdgcn_exp2f(m - mn);
-      acc_l[i] = acc_l[i] * a + l * sc;
-      acc_o[i] = acc_o[i] * a + __builtin_bit_cast(f32x4_t, R.o[i]) * sc;
-      acc_m[i] = mn;
+      lse_combine(acc_m[i], acc_l[i], acc_o[i], __builtin_bit_cast(float, R.m[i]),
+                  __builtin_bit_cast(float, R.l[i]), __builtin_bit_cast(f32x4_t, R.o[i]));
     }
   };
   PieceRegs R[PB];
@@ -339,12 +349,7 @@ __device__ __forceinline__ void merge_with_own(const Params& p, OutT* out, int n
     acc_o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   auto merge_vals = [&](int i, float m, float l, f32x4_t o) __attribute__((always_inline)) {
-    const float mn = fmaxf(acc_m[i], m);
-    const float a = __builtin_amdgcn_exp2f(acc_m[i] - mn);
-    const float sc = __builtin_amdgcn_exp2f(m - mn);
-    acc_l[i] = acc_l[i] * a + l * sc;
-    acc_o[i] = acc_o[i] * a + o * sc;
-    acc_m[i] = mn;
+    lse_combine(acc_m[i], acc_l[i], acc_o[i], m, l, o);
   };
   // pieces in workgroup order: k = 0 .. npc - 1, the own one at own_k
 #pragma unroll
@@ -393,9 +398,13 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
     o = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
+      // explicit fused multiply-adds: the publishing and the merging epilogues inline this at
+      // different sites and must round alike
       const float s = __builtin_amdgcn_exp2f(ep_m[w * GT + g] - M);
-      l += s * ep_l[w * GT + g];
-      o += s * *reinterpret_cast<const f32x4_t*>(ep_o + (w * GT + g) * kRow + cc);
+      l = __builtin_fmaf(s, ep_l[w * GT + g], l);
+      const f32x4_t x = *reinterpret_cast<const f32x4_t*>(ep_o + (w * GT + g) * kRow + cc);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = __builtin_fmaf(s, x[c], o[c]);
     }
   };
 
