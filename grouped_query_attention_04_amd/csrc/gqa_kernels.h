@@ -62,6 +62,11 @@ struct Params {
 // fills its output rows with NaN and counts itself in header word 2 instead of touching a counter.
 constexpr uint32_t kWorkspaceTag0 = 0x41514721u, kWorkspaceTag1 = 0x5EED0C7Au;
 constexpr int kWorkspaceHeaderWords = 64;  // 256 bytes before the counter area
+// Header word 3 holds merge-route flags for tests (zero after initialisation): bit 0 publishes every
+// shared piece (the merge from registers of a segment's last piece is off), bit 1 counts the merges
+// from registers in header word 4.  The output does not depend on them.
+constexpr int kRouteFlagsWord = 3, kShortcutCountWord = 4;
+constexpr uint32_t kRouteAlwaysPublish = 1u, kRouteCountShortcuts = 2u;
 
 // Both tag words, read with scalar loads; the caller compares them later, so the load's latency
 // overlaps with whatever comes in between.
@@ -377,7 +382,7 @@ __device__ __forceinline__ void merge_with_own(const Params& p, OutT* out, int n
 
 template <int GT, int D, int NW, typename OutT>
 __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r, const Piece& pc,
-                               Shared& sh, bool known_last = false) {
+                               Shared& sh, bool known_last = false, uint32_t route_flags = 0) {
   constexpr int NTH = NW * 64;
   constexpr int kRow = EpiLayout<GT, D, NW>::kRow;
   const int tid = threadIdx.x;
@@ -442,7 +447,11 @@ __device__ void piece_epilogue(const Params& p, const float* ep, const Range& r,
     const int first_slot = uniform(pc.s > range_lo(wfirst, r.T, r.weff) ? 1 : 0);
     merge_with_own<D, OutT, NTH, NI>(p, out, nitems, wfirst, wlast - wfirst + 1, first_slot,
                                      (int)blockIdx.x - wfirst, own_m, own_l, own_o);
-    if (tid == 0) __hip_atomic_store(p.counters + pc.b * p.Hkv + pc.j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_store(p.counters + pc.b * p.Hkv + pc.j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (route_flags & kRouteCountShortcuts)
+        __hip_atomic_fetch_add(p.header + kShortcutCountWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     return;
   }
 
@@ -893,7 +902,10 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
     //      workgroups finish: 142.8 -> 141.5 us).  One query tile only: with four, the registers of
     //      the extra merge would spill.
     const int sg_first = range_owner(pc.s, rg.T, rg.weff), sg_last = range_owner(pc.e - 1, rg.T, rg.weff);
-    const bool sg_check = NT == 1 && sg_first != sg_last && sg_last - sg_first <= 2;
+    // the merge-route flags of the workspace header (a scalar load, cached)
+    const uint32_t route_flags = ((const GQA_CONST uint32_t*)(uintptr_t)p.header)[kRouteFlagsWord];
+    const bool sg_check = NT == 1 && sg_first != sg_last && sg_last - sg_first <= 2 &&
+                          !(route_flags & kRouteAlwaysPublish);
     uint32_t arrived = 0;
     if (sg_check && threadIdx.x == 0)
       arrived = __hip_atomic_load(p.counters + pc.b * p.Hkv + pc.j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -916,7 +928,7 @@ __global__ void __launch_bounds__(NW * 64, NT == 1 ? 2 : 1) decode_mfma_kernel(P
     __syncthreads();
     const bool known_last = NT == 1 && uniform(sh.last);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    piece_epilogue<GT, D, NW, OutT>(p, ep, rg, pc, sh, known_last);
+    piece_epilogue<GT, D, NW, OutT>(p, ep, rg, pc, sh, known_last, route_flags);
     __syncthreads();  // the epilogue's LDS reads finish before the next piece writes V tiles
   });
 }

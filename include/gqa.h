@@ -83,7 +83,10 @@ gqa_status_t gqa_shape_check(const gqa_shape_t* shape);
  * per workgroup.  0 if the shape is invalid.  Host only.
  *
  * Header: bytes 0-7 hold a tag that only gqa_workspace_init writes; bytes 8-11 are a uint32 error
- * count.  The merge of a (batch, KV head) segment that several workgroups share is done by the one
+ * count.  Bytes 12-15 (uint32, zero after initialisation) are merge-route flags for tests: bit 0
+ * makes every workgroup publish its piece of a shared segment, never merging the last piece from
+ * registers; bit 1 makes the decodes count, in bytes 16-19, the segments merged from registers.
+ * The output is bitwise the same for any value of the flags.  The merge of a (batch, KV head) segment that several workgroups share is done by the one
  * that finishes last, found with the segment's counter, so the counters must start at zero. */
 size_t gqa_decode_workspace_bytes(const gqa_shape_t* shape);
 

@@ -407,6 +407,44 @@ def test_merge_soak_is_bitwise_stable(cfg):
     assert (ws[8:COUNTERS_END] == 0).all()
 
 
+ROUTES = [(32, 64, 8, 128, 1024, "bf16"), (16, 32, 8, 128, 1500, "fp8_e4m3"), (16, 32, 1, 128, 700, "bf16"),
+          (24, 16, 2, 64, 900, "bf16"), (48, 40, 8, 128, 600, "bf16")]
+ROUTE_FLAGS_WORD, SHORTCUT_COUNT_WORD = 3, 4  # workspace header words (include/gqa.h)
+ALWAYS_PUBLISH, COUNT_SHORTCUTS = 1, 2
+
+
+def test_merge_routes_agree_bitwise():
+    """A segment of two or three pieces is merged either by the last workgroup from its registers
+    (when it finds the other pieces already counted) or from the published partials; which one runs
+    depends on timing.  Both must give the same bits: each shape is decoded ten times with the
+    register route allowed (and counted through the workspace header's test flags) and ten times with
+    every piece published, and all twenty outputs must be bitwise one.  The register route has to
+    have run at least once over the shapes, and never under the publish-only flag."""
+    taken = 0
+    for cfg in ROUTES:
+        B, Hq, Hkv, d, L, kd = cfg
+        say(f"merge routes {cfg}")
+        case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", kd, seq_range=(L // 3, L), seed=B * L + Hq)
+        dv = to_dev(case)
+        shape = gqa.make_shape(B, Hq, Hkv, L, d, gqa.BF16, gqa._CODE[TORCH[kd]], gqa.F32)
+        outs, counts = [], []
+        for flags in (COUNT_SHORTCUTS, ALWAYS_PUBLISH | COUNT_SHORTCUTS):
+            ws = gqa.new_workspace(shape, DEV)
+            words = ws.view(torch.int32)
+            words[ROUTE_FLAGS_WORD] = flags
+            outs += [gqa.decode(dv["q"], dv["k"], dv["v"], dv["seq_lens"], case["scale"],
+                                out_dtype=torch.float32, workspace=ws) for _ in range(10)]
+            torch.cuda.synchronize()
+            counts.append(int(words[SHORTCUT_COUNT_WORD].item()))
+        say(f"  merges from registers: {counts[0]} (route allowed), {counts[1]} (publish only)")
+        assert counts[1] == 0
+        taken += counts[0]
+        for i, o in enumerate(outs[1:], 1):
+            assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32)), f"{cfg}: run {i} differs"
+        compare(outs[0], oracle_full(case), kd, "routes")
+    assert taken > 0, "no segment was merged from registers"
+
+
 def test_out_of_range_seq_lens_are_clamped_and_reported():
     say("seq_len clamp")
     L = 400
