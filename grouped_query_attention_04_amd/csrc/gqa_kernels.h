@@ -941,6 +941,12 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
   constexpr int TILE = 64;
   constexpr int NTH = NW * 64;
   constexpr int CPL = D / 64;  // output columns per lane
+  // loads in flight per lane: a whole key row (KL 16-byte loads) and VL value rows at a time when the
+  // group is small (each tile's work is then a chain of load round trips: a tiny step is 16.8 us
+  // with eight of each in flight), eight of each otherwise, where the registers hold the group's
+  // scores and outputs.  The arithmetic and its order do not depend on them.
+  constexpr int KL = GT <= 4 ? D / 4 : 8;
+  constexpr int VL = GT <= 4 ? 32 : 8;
   using Epi = EpiLayout<GT, D, NW>;
   constexpr int QB = GT * D * 4;
   constexpr int PB = NW * GT * TILE * 4;
@@ -991,14 +997,14 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
 #pragma unroll
       for (int g = 0; g < GT; ++g) s[g] = 0.f;
       if (valid) {
-        // this lane's key row, eight 16-byte loads in flight at a time
+        // this lane's key row, KL 16-byte loads in flight at a time
         const float4* kr = reinterpret_cast<const float4*>(kh + (size_t)t * D);
-        for (int c0 = 0; c0 < D / 4; c0 += 8) {
-          float4 kv[8];
+        for (int c0 = 0; c0 < D / 4; c0 += KL) {
+          float4 kv[KL];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) kv[u] = kr[c0 + u];
+          for (int u = 0; u < KL; ++u) kv[u] = kr[c0 + u];
 #pragma unroll
-          for (int u = 0; u < 8; ++u)
+          for (int u = 0; u < KL; ++u)
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
               const float4 qv = *reinterpret_cast<const float4*>(qs + g * D + 4 * (c0 + u));
@@ -1021,18 +1027,18 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
         for (int x = 0; x < CPL; ++x) o[g][x] *= alpha;
         ps[g * TILE + l] = pw;
       }
-      // value rows in groups of eight, their loads in flight together (rows past the tile's last
+      // value rows in groups of VL, their loads in flight together (rows past the tile's last
       // position are not read)
       const int cnt = min(TILE, n - t0);
-      for (int t8 = 0; t8 < cnt; t8 += 8) {
-        float vv[8][CPL];
+      for (int t8 = 0; t8 < cnt; t8 += VL) {
+        float vv[VL][CPL];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < VL; ++u)
 #pragma unroll
           for (int x = 0; x < CPL; ++x)
             vv[u][x] = t8 + u < cnt ? vh[(size_t)(t0 + t8 + u) * D + 64 * x + l] : 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < VL; ++u) {
           if (t8 + u >= cnt) break;
 #pragma unroll
           for (int g = 0; g < GT; ++g) {
