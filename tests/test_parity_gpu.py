@@ -646,3 +646,19 @@ def test_batches_above_256(B, wg, kd):
     for b, n in enumerate(sl):
         if n == 0:
             assert (got[b] == 0).all(), b
+
+
+def test_largest_unit_count_the_abi_takes():
+    """2^18 (batch, KV head) pairs, the most the workspace's counter area holds (32,768 sequences of
+    eight KV heads, lengths drawn from 0 to 32, so segments have zero, one or two tiles and the
+    boundaries of the 256 workgroups' ranges cut some of them, up to counters near the end of the
+    area), through the range search's 128 passes: every row against the oracle, empty sequences
+    zero.  One pair more is refused on the host (the boundary tests)."""
+    B, Hq, Hkv, d, L = 32768, 8, 8, 64, 32
+    assert B * Hkv == 1 << 18
+    say("2^18 (batch, KV head) pairs")
+    case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", "bf16", seq_range=(0, L), seed=18)
+    got = run(case, out_dtype="f32")
+    compare(got, oracle_full(case), "bf16", "2^18 pairs")
+    empty = (case["seq_lens"] == 0).numpy()
+    assert empty.any() and (got.cpu()[torch.from_numpy(empty)] == 0).all()
