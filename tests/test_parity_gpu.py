@@ -648,6 +648,20 @@ def test_batches_above_256(B, wg, kd):
             assert (got[b] == 0).all(), b
 
 
+def test_most_workgroups_the_abi_takes():
+    """65,536 workgroups, the most the C ABI accepts, on a tile space larger than that (64 sequences
+    of 2,048 to 4,096 positions, eight KV heads: about 98,000 tiles of 16 positions), so every
+    workgroup takes one or two tiles, each (batch, KV head) segment is cut into over a hundred pieces
+    and merged from them, and the range bounds w * T / W pass 2^32: every row against the oracle."""
+    B, Hq, Hkv, d, L, W = 64, 64, 8, 128, 4096, 65536
+    say(f"{W} workgroups")
+    case = workloads.make_case(B, Hq, Hkv, d, L, "bf16", "bf16", seq_range=(L // 2, L), seed=65536)
+    tiles = int(((case["seq_lens"] + 15) // 16).sum()) * Hkv
+    assert tiles > W
+    got = run(case, out_dtype="f32", workgroups=W)
+    compare(got, oracle_full(case), "bf16", f"{W} workgroups, {tiles} tiles")
+
+
 def test_largest_unit_count_the_abi_takes():
     """2^18 (batch, KV head) pairs, the most the workspace's counter area holds (32,768 sequences of
     eight KV heads, lengths drawn from 0 to 32, so segments have zero, one or two tiles and the
