@@ -941,12 +941,13 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
   constexpr int TILE = 64;
   constexpr int NTH = NW * 64;
   constexpr int CPL = D / 64;  // output columns per lane
-  // loads in flight per lane: a whole key row (KL 16-byte loads) and VL value rows at a time when the
-  // group is small (each tile's work is then a chain of load round trips: a tiny step is 16.8 us
-  // with eight of each in flight), eight of each otherwise, where the registers hold the group's
-  // scores and outputs.  The arithmetic and its order do not depend on them.
-  constexpr int KL = GT <= 4 ? D / 4 : 8;
-  constexpr int VL = GT <= 4 ? 32 : 8;
+  // loads in flight per lane: a whole key row (KL 16-byte loads) and VL value rows at a time for a
+  // small group at head dim 64 (each tile's work is then a chain of load round trips: a tiny step is
+  // 16.8 us with eight of each in flight), eight of each otherwise (at head dim 128 the larger sets
+  // are not fully unrolled and land in scratch).  The arithmetic and its order do not depend on them.
+  constexpr bool kWide = GT <= 4 && D == 64;
+  constexpr int KL = kWide ? D / 4 : 8;
+  constexpr int VL = kWide ? 32 : 8;
   using Epi = EpiLayout<GT, D, NW>;
   constexpr int QB = GT * D * 4;
   constexpr int PB = NW * GT * TILE * 4;
@@ -1039,7 +1040,11 @@ __global__ void __launch_bounds__(NW * 64) decode_f32_kernel(Params p) {
             vv[u][x] = t8 + u < cnt ? vh[(size_t)(t0 + t8 + u) * D + 64 * x + l] : 0.f;
 #pragma unroll
         for (int u = 0; u < VL; ++u) {
-          if (t8 + u >= cnt) break;
+          // rows past the tile's last position: with the wide sets they are not skipped (the loop
+          // then unrolls) and add fma(0, 0, o) = o, as their weights and value registers are zero
+          if constexpr (!kWide) {
+            if (t8 + u >= cnt) break;
+          }
 #pragma unroll
           for (int g = 0; g < GT; ++g) {
             const float pw = ps[g * TILE + t8 + u];
